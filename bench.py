@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark: one EP-MoE layer forward (all five stages) on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic tokens:
+select_experts -> pre_reorder_quant -> grouped GEMM (w13) -> act_requant ->
+grouped GEMM (w2) -> post_reorder, enqueued on one stream. Inputs and weights
+are resident in HBM before the timed region. The default workload is the
+DeepSeek-V3-shaped prefill share of one GPU in an 8-way expert-parallel layer
+(T=8192 tokens, 32 of 256 experts local), the configuration the grouped-GEMM
+target is stated for.
+
+Prints one JSON line: whole-job tokens/s, the dominant kernel's roofline
+figures (HIP events around every launch inside the timed region) and the CPU
+oracle's tokens/s on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+METRIC = "EP-MoE layer tokens/s at 1 GPU; grouped FP8 GEMM TFLOP/s as % of MFMA peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="dsv3_prefill_ep")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=0,
+                   help="tokens in the oracle's timed sample (0: per-workload default)")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="after the run, copy this many MiB once (a plain copy kernel for counter calibration)")
+    return p.parse_args()
+
+
+def algorithmic_work(cfg, seg, a_scale_bytes13, a_scale_bytes2, w13_scale_numel, w2_scale_numel):
+    """Bytes each stage must move (inputs read once, outputs written once) and GEMM FLOPs."""
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk
+    M = int(seg[-1])
+    counts = np.diff(seg)
+    nonempty = int((counts > 0).sum())
+    El = cfg.num_local
+    b13 = nonempty * 2 * I * H + w13_scale_numel * 4 * nonempty // max(El, 1)
+    b2 = nonempty * H * I + w2_scale_numel * 4 * nonempty // max(El, 1)
+    tok_local = None
+    work = {}
+    work["select"] = dict(bytes=T * E * 4 + (E * 4 if cfg.use_bias else 0) + T * k * 8, flops=0)
+    # pre_reorder: ids + x rows of tokens with a local pair (+ a second read of x for the
+    # per-tensor amax), codes + scales of M rows, src2dst / dst2src / seg
+    work["pre_reorder"] = dict(bytes=T * k * 4 + T * H * 2 * (2 if cfg.act_quant == 0 else 1)
+                               + M * H + a_scale_bytes13 + T * k * 4 + cfg.m_cap * 4 + (El + 1) * 4,
+                               flops=0)
+    work["gemm_w13"] = dict(bytes=M * H + a_scale_bytes13 + b13 + M * 2 * I * 2 + (El + 1) * 4,
+                            flops=2 * M * (2 * I) * H)
+    work["act_requant"] = dict(bytes=M * 2 * I * 2 * (2 if cfg.act_quant == 0 else 1) + M * I
+                               + a_scale_bytes2, flops=0)
+    work["gemm_w2"] = dict(bytes=M * I + a_scale_bytes2 + b2 + M * H * 2 + (El + 1) * 4,
+                           flops=2 * M * H * I)
+    work["post_reorder"] = dict(bytes=M * H * 2 + T * k * 8 + T * H * 2, flops=0)
+    return work, M, nonempty
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import fp8_grouped_gemm_select_amd as moe
+    import workloads as W
+
+    cfg = W.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    inp = W.gen_layer_inputs(cfg, seed=args.seed)
+
+    def up(a, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dtype is not None:
+            t = t.view(dtype)
+        return t.to(dev)
+
+    x = up(inp.x.view(np.int16), torch.bfloat16)
+    logits = up(inp.logits)
+    bias = up(inp.bias) if inp.bias is not None else None
+    w13, s13 = up(inp.w13), up(inp.w13_scale.reshape(-1))
+    w2, s2 = up(inp.w2), up(inp.w2_scale.reshape(-1))
+    buf = moe.LayerBuffers.allocate(cfg.T, cfg.H, cfg.I, cfg.topk, cfg.num_local, cfg.act_quant)
+    gen_s = time.time() - t0
+    print(f"[bench] {cfg.name}: inputs ready in {gen_s:.1f}s", file=sys.stderr, flush=True)
+
+    kw = dict(topk=cfg.topk, n_group=cfg.n_group, topk_group=cfg.topk_group,
+              score_fn=cfg.score_fn, renormalize=cfg.renormalize,
+              routed_scaling_factor=cfg.rsf, apply_rsf=cfg.apply_rsf,
+              expert_start=cfg.expert_start, num_local=cfg.num_local, act_quant=cfg.act_quant,
+              w_quant=cfg.w_quant)
+    stages = ["select", "pre_reorder", "gemm_w13", "act_requant", "gemm_w2", "post_reorder"]
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record()
+        mark(0)
+        moe.moe_select_experts(logits, bias, buf.topk_ids, buf.topk_weights, topk=cfg.topk,
+                               n_group=cfg.n_group, topk_group=cfg.topk_group,
+                               score_fn=cfg.score_fn, renormalize=cfg.renormalize,
+                               routed_scaling_factor=cfg.rsf, apply_rsf=cfg.apply_rsf)
+        mark(1)
+        moe.moe_pre_reorder_quant(x, buf.topk_ids, buf.a13, buf.a13_scale, buf.src2dst,
+                                  buf.dst2src, buf.seg_indptr, buf.workspace,
+                                  expert_start=cfg.expert_start, num_local=cfg.num_local,
+                                  act_quant=cfg.act_quant)
+        mark(2)
+        moe.moe_grouped_gemm_fp8(buf.a13, buf.a13_scale, w13, s13, buf.seg_indptr, buf.c13,
+                                 act_quant=cfg.act_quant, w_quant=cfg.w_quant)
+        mark(3)
+        moe.moe_act_requant(buf.c13, buf.seg_indptr, buf.a2, buf.a2_scale, buf.workspace,
+                            act_quant=cfg.act_quant)
+        mark(4)
+        moe.moe_grouped_gemm_fp8(buf.a2, buf.a2_scale, w2, s2, buf.seg_indptr, buf.c2,
+                                 act_quant=cfg.act_quant, w_quant=cfg.w_quant)
+        mark(5)
+        moe.moe_post_reorder(buf.c2, buf.src2dst, buf.topk_weights, buf.out)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` layer passes; HIP events on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+                for i, name in enumerate(stages)}
+
+    seg = buf.seg_indptr.cpu().numpy()
+    work, M, nonempty = algorithmic_work(cfg, seg, buf.a13_scale.numel() * 4, buf.a2_scale.numel() * 4,
+                                         s13.numel(), s2.numel())
+    stage_stats = {}
+    for name in stages:
+        t = stage_ms[name] * 1e-3
+        b, f = work[name]["bytes"], work[name]["flops"]
+        stage_stats[name] = dict(us=round(stage_ms[name] * 1e3, 2), GBps=round(b / t / 1e9, 1),
+                                 hbm_frac=round(b / t / 1e9 / HBM_PEAK_GBS, 4))
+        if f:
+            stage_stats[name].update(TFLOPs=round(f / t / 1e12, 1),
+                                     mfma_frac=round(f / t / 1e12 / FP8_PEAK_TFLOPS, 4))
+    dom = max(stages, key=lambda n: stage_ms[n])
+    db, df = work[dom]["bytes"], work[dom]["flops"]
+    dt = stage_ms[dom] * 1e-3
+    hbm_time = db / (HBM_PEAK_GBS * 1e9)
+    mfma_time = df / (FP8_PEAK_TFLOPS * 1e12) if df else 0.0
+    if mfma_time > hbm_time:
+        roof = dict(bound="mfma", achieved=round(df / dt / 1e12, 2), peak=FP8_PEAK_TFLOPS,
+                    unit="TFLOP/s")
+    else:
+        roof = dict(bound="hbm", achieved=round(db / dt / 1e9, 1), peak=HBM_PEAK_GBS, unit="GB/s")
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = int(db)
+    roof["algorithmic_flops"] = int(df)
+    roof["traffic"] = None
+    gemm_t = (stage_ms["gemm_w13"] + stage_ms["gemm_w2"]) * 1e-3
+    gemm_f = work["gemm_w13"]["flops"] + work["gemm_w2"]["flops"]
+    gemm = dict(tflops=round(gemm_f / gemm_t / 1e12, 1),
+                frac_of_fp8_peak=round(gemm_f / gemm_t / 1e12 / FP8_PEAK_TFLOPS, 4),
+                w13_tflops=stage_stats["gemm_w13"].get("TFLOPs"),
+                w2_tflops=stage_stats["gemm_w2"].get("TFLOPs"))
+
+    tokens_per_s = cfg.T / (ms_per_step * 1e-3)
+    result = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+                   "topk": cfg.topk, "num_local": cfg.num_local, "M": M,
+                   "experts_with_rows": nonempty, "act_quant": cfg.act_quant,
+                   "w_quant": cfg.w_quant, "parallelism": "single GPU (one EP share)"},
+        "roofline": roof, "gemm": gemm, "stages": stage_stats,
+    }
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = n
+        del src, dst
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, inp, sample_tokens):
+    """The oracle, as it stands, on the first `sample_tokens` tokens of the same workload."""
+    import dataclasses
+    import oracle
+    import workloads as W
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    if not sample_tokens:
+        sample_tokens = {"tiny": 16, "dsv3_decode_ep": 128, "dsv3_prefill_ep": 512,
+                         "mixtral": 64, "skewed_block": 512}.get(cfg.name, 256)
+    Ts = min(sample_tokens, cfg.T)
+    sub = dataclasses.replace(inp, cfg=dataclasses.replace(cfg, T=Ts), x=inp.x[:Ts],
+                              logits=inp.logits[:Ts])
+    t0 = time.perf_counter()
+    oracle.layer(sub)
+    dt = time.perf_counter() - t0
+    return {"value": round(Ts / dt, 2), "unit": "tokens/s", "cores": oracle.get_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {Ts} of {cfg.T} tokens of {cfg.name}, full expert weights, "
+                      f"whole layer (routing, permutation, both GEMMs, activation, combine)"}
+
+
+if __name__ == "__main__":
+    main()

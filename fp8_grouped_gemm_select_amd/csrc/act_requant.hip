@@ -1,0 +1,228 @@
+// Stage 4: SiLU(gate) * up rounded to bf16, then dynamic FP8 requantisation of
+// the w2 input, one wavefront per row over the M rows that exist on the device.
+//
+// Follows "Support token-level quantization for EP MoE" (sglang PR #6782),
+// change summary of layer.py: down_input comes out of the activation in the
+// activation dtype and is then quantised per token, giving w2_input_scale.
+//
+// Per row and per 128-column group the whole step is one pass (h stays in
+// registers between the amax and the encode for rows up to 8192 wide). The
+// per-tensor mode needs the maximum over all M*I values first: pass 1 writes a
+// partial maximum per block, pass 2 reduces the partials in every block and
+// recomputes h while encoding (re-reading gate/up costs the same bytes as
+// storing and re-reading h).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRegIters = 8;
+constexpr int kActBlocks = 2048;  // fixed grid of the per-tensor passes (partials buffer)
+
+struct ActWs {
+    float* part;  // [kActBlocks]
+};
+
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+__device__ __forceinline__ int64_t rows_present(const int32_t* seg, int num_local, int64_t m_cap) {
+    int64_t M = seg[num_local];
+    return M < 0 ? 0 : (M > m_cap ? m_cap : M);
+}
+
+// h for 16 consecutive columns [c, c+16) of `row` (packed bf16 pairs), zeros past I.
+__device__ __forceinline__ void silu_mul16(const uint16_t* __restrict__ gu, int64_t row, int I, int c,
+                                           uint4& h0, uint4& h1) {
+    if (c >= I) {
+        h0 = make_uint4(0, 0, 0, 0);
+        h1 = h0;
+        return;
+    }
+    const uint4* g4 = (const uint4*)(gu + row * 2 * (int64_t)I + c);
+    const uint4* u4 = (const uint4*)(gu + row * 2 * (int64_t)I + I + c);
+    const uint4 ga = g4[0], gb = g4[1], ua = u4[0], ub = u4[1];
+    const uint32_t g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+    const uint32_t u[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+    uint32_t h[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float g0 = bf16_lo(g[q]), g1 = bf16_hi(g[q]);
+        const float u0 = bf16_lo(u[q]), u1 = bf16_hi(u[q]);
+        const float s0 = g0 / (1.0f + exp_fixed(-g0));
+        const float s1 = g1 / (1.0f + exp_fixed(-g1));
+        h[q] = f32_to_bf16_bits(s0 * u0) | (f32_to_bf16_bits(s1 * u1) << 16);
+    }
+    h0 = make_uint4(h[0], h[1], h[2], h[3]);
+    h1 = make_uint4(h[4], h[5], h[6], h[7]);
+}
+
+__device__ __forceinline__ float amax16(const uint4& a, const uint4& b) {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[q])), fabsf(bf16_hi(w[q]))));
+    return m;
+}
+
+__device__ __forceinline__ uint4 quant16(const uint4& a, const uint4& b, float inv) {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        o[q] = quant4(bf16_lo(w[2 * q]), bf16_hi(w[2 * q]), bf16_lo(w[2 * q + 1]), bf16_hi(w[2 * q + 1]), inv);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+template <int MODE>  // MOE_ACT_PER_TOKEN or MOE_ACT_PER_GROUP
+__global__ __launch_bounds__(256) void act_requant_kernel(const uint16_t* __restrict__ gu,
+                                                          const int32_t* __restrict__ seg,
+                                                          int num_local, int64_t m_cap, int I,
+                                                          uint8_t* __restrict__ a_q,
+                                                          float* __restrict__ a_scale) {
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t M = rows_present(seg, num_local, m_cap);
+    const int nit = (I + 1023) / 1024;
+    const int G = (I + MOE_QB - 1) / MOE_QB;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + wid; row < M; row += (int64_t)gridDim.x * 4) {
+        uint8_t* out = a_q + row * I;
+        if (MODE == MOE_ACT_PER_GROUP) {
+            for (int it = 0; it < nit; ++it) {
+                const int c = it * 1024 + lane * 16;
+                uint4 h0, h1;
+                silu_mul16(gu, row, I, c, h0, h1);
+                float s, inv;
+                dyn_scale(group8_max(amax16(h0, h1)), s, inv);
+                if (c < I) *(uint4*)(out + c) = quant16(h0, h1, inv);
+                const int g = it * 8 + (lane >> 3);
+                if ((lane & 7) == 0 && g < G) a_scale[row * G + g] = s;
+            }
+            continue;
+        }
+        uint4 hb[kRegIters][2];
+        float amax = 0.0f;
+#pragma unroll
+        for (int it = 0; it < kRegIters; ++it)
+            if (it < nit) {
+                silu_mul16(gu, row, I, it * 1024 + lane * 16, hb[it][0], hb[it][1]);
+                amax = fmaxf(amax, amax16(hb[it][0], hb[it][1]));
+            }
+        for (int it = kRegIters; it < nit; ++it) {
+            uint4 h0, h1;
+            silu_mul16(gu, row, I, it * 1024 + lane * 16, h0, h1);
+            amax = fmaxf(amax, amax16(h0, h1));
+        }
+        float s, inv;
+        dyn_scale(wave_max(amax), s, inv);
+#pragma unroll
+        for (int it = 0; it < kRegIters; ++it) {
+            const int c = it * 1024 + lane * 16;
+            if (it < nit && c < I) *(uint4*)(out + c) = quant16(hb[it][0], hb[it][1], inv);
+        }
+        for (int it = kRegIters; it < nit; ++it) {
+            const int c = it * 1024 + lane * 16;
+            uint4 h0, h1;
+            silu_mul16(gu, row, I, c, h0, h1);
+            if (c < I) *(uint4*)(out + c) = quant16(h0, h1, inv);
+        }
+        if (lane == 0) a_scale[row] = s;
+    }
+}
+
+// per tensor, pass 1: partial maxima of |h|
+__global__ __launch_bounds__(256) void act_amax_kernel(const uint16_t* __restrict__ gu,
+                                                       const int32_t* __restrict__ seg, int num_local,
+                                                       int64_t m_cap, int I, float* __restrict__ part) {
+    __shared__ float red[4];
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t M = rows_present(seg, num_local, m_cap);
+    const int nit = (I + 1023) / 1024;
+    float amax = 0.0f;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + wid; row < M; row += (int64_t)gridDim.x * 4)
+        for (int it = 0; it < nit; ++it) {
+            uint4 h0, h1;
+            silu_mul16(gu, row, I, it * 1024 + lane * 16, h0, h1);
+            amax = fmaxf(amax, amax16(h0, h1));
+        }
+    amax = wave_max(amax);
+    if (lane == 0) red[wid] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// per tensor, pass 2: every block reduces the partials, then encodes its rows
+__global__ __launch_bounds__(256) void act_quant_tensor_kernel(const uint16_t* __restrict__ gu,
+                                                               const int32_t* __restrict__ seg,
+                                                               int num_local, int64_t m_cap, int I,
+                                                               const float* __restrict__ part,
+                                                               int n_part, uint8_t* __restrict__ a_q,
+                                                               float* __restrict__ a_scale) {
+    __shared__ float red[4];
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < n_part; i += 256) m = fmaxf(m, part[i]);
+    m = wave_max(m);
+    if (lane == 0) red[wid] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float s, inv;
+    dyn_scale(amax, s, inv);
+    if (blockIdx.x == 0 && threadIdx.x == 0) a_scale[0] = s;
+    const int64_t M = rows_present(seg, num_local, m_cap);
+    const int nit = (I + 1023) / 1024;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + wid; row < M; row += (int64_t)gridDim.x * 4)
+        for (int it = 0; it < nit; ++it) {
+            const int c = it * 1024 + lane * 16;
+            uint4 h0, h1;
+            silu_mul16(gu, row, I, c, h0, h1);
+            if (c < I) *(uint4*)(a_q + row * I + c) = quant16(h0, h1, inv);
+        }
+}
+
+}  // namespace
+
+size_t act_requant_ws_bytes() { return align256(sizeof(float) * kActBlocks); }
+
+}  // namespace moe
+
+extern "C" int moe_act_requant(const void* gateup_bf16, const int32_t* seg_indptr, int32_t num_local,
+                               int64_t m_cap, int32_t I, int32_t act_quant, uint8_t* a_q,
+                               float* a_scale, int64_t a_scale_numel, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    using namespace moe;
+    if (num_local < 0 || m_cap < 0 || I <= 0) return MOE_ERR_INVALID_ARG;
+    if (act_quant < MOE_ACT_PER_TENSOR || act_quant > MOE_ACT_PER_GROUP) return MOE_ERR_INVALID_ARG;
+    if (I % 16 != 0) return MOE_ERR_UNSUPPORTED;
+    if (m_cap * (int64_t)I > ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+    const int64_t G = ceil_div(I, MOE_QB);
+    const int64_t want = act_quant == MOE_ACT_PER_TENSOR ? 1 : act_quant == MOE_ACT_PER_TOKEN ? m_cap : m_cap * G;
+    if (a_scale_numel != want) return MOE_ERR_SHAPE;
+    if (!seg_indptr) return MOE_ERR_NULL;
+    if (act_quant == MOE_ACT_PER_TENSOR && (!workspace || workspace_bytes < act_requant_ws_bytes()))
+        return MOE_ERR_WORKSPACE;
+    if (m_cap == 0 && act_quant != MOE_ACT_PER_TENSOR) return MOE_OK;
+    if (!a_scale || (m_cap > 0 && (!gateup_bf16 || !a_q))) return MOE_ERR_NULL;
+    if ((gateup_bf16 && !aligned16(gateup_bf16)) || (a_q && !aligned16(a_q))) return MOE_ERR_INVALID_ARG;
+
+    (void)hipGetLastError();
+    hipStream_t s = (hipStream_t)stream;
+    const uint16_t* gu = (const uint16_t*)gateup_bf16;
+    if (act_quant == MOE_ACT_PER_TENSOR) {
+        float* part = (float*)workspace;
+        hipLaunchKernelGGL(act_amax_kernel, dim3(kActBlocks), dim3(256), 0, s, gu, seg_indptr,
+                           num_local, m_cap, I, part);
+        hipLaunchKernelGGL(act_quant_tensor_kernel, dim3(kActBlocks), dim3(256), 0, s, gu,
+                           seg_indptr, num_local, m_cap, I, part, kActBlocks, a_q, a_scale);
+        return launch_status();
+    }
+    int64_t grid = ceil_div(m_cap, 4);
+    const int64_t cap = (int64_t)device_cu_count() * 16;
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    if (act_quant == MOE_ACT_PER_TOKEN)
+        hipLaunchKernelGGL(act_requant_kernel<MOE_ACT_PER_TOKEN>, dim3((unsigned)grid), dim3(256), 0,
+                           s, gu, seg_indptr, num_local, m_cap, I, a_q, a_scale);
+    else
+        hipLaunchKernelGGL(act_requant_kernel<MOE_ACT_PER_GROUP>, dim3((unsigned)grid), dim3(256), 0,
+                           s, gu, seg_indptr, num_local, m_cap, I, a_q, a_scale);
+    return launch_status();
+}

@@ -1,0 +1,144 @@
+// Device helpers shared by the libmoe kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+#define MOE_WAVE 64
+#define MOE_E4M3_MAX 448.0f
+#define MOE_QB 128  // block / group size of block quantisation
+
+namespace moe {
+
+// ---- host-side launch helpers ------------------------------------------------
+
+static inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static inline int launch_status() {
+    hipError_t err = hipGetLastError();
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int device_cu_count();  // compute units of the current device (cached per device)
+
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- exact-math helpers (the fp32 operation sequence is part of the contract) --
+
+#pragma clang fp contract(off)
+
+// exp(x) in fp32 with a fixed sequence: clamp to [-80, 80]; n = rint(x*log2 e);
+// two-constant Cody-Waite reduction r = x - n*ln2 (one fma each); degree-7
+// Taylor polynomial in Horner form (one fma per step); scale by 2^n.
+__device__ __forceinline__ float exp_fixed(float x) {
+    x = fminf(fmaxf(x, -80.0f), 80.0f);
+    const float n = __builtin_rintf(x * 1.44269504088896341f);
+    float r = __builtin_fmaf(-n, 0.693145751953125f, x);
+    r = __builtin_fmaf(-n, 1.42860682030941723212e-6f, r);
+    float p = (float)(1.0 / 5040.0);
+    p = __builtin_fmaf(p, r, (float)(1.0 / 720.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 120.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 24.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 6.0));
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float sigmoid_fixed(float x) { return 1.0f / (1.0f + exp_fixed(-x)); }
+
+// bf16 <-> fp32 (round to nearest even for finite values).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float v) {
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Dynamic FP8 scale: s = max(amax,1e-10)/448 (stored), inv = 448/max(amax,1e-10) (applied).
+__device__ __forceinline__ void dyn_scale(float amax, float& scale, float& inv) {
+    const float a = amax > 1e-10f ? amax : 1e-10f;
+    scale = a / MOE_E4M3_MAX;
+    inv = MOE_E4M3_MAX / a;
+}
+
+// Four fp32 values -> four OCP e4m3 codes packed little-endian, after x*inv and
+// saturation to +-448 (the conversion rounds to nearest even).
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float inv) {
+    a = fminf(fmaxf(a * inv, -MOE_E4M3_MAX), MOE_E4M3_MAX);
+    b = fminf(fmaxf(b * inv, -MOE_E4M3_MAX), MOE_E4M3_MAX);
+    c = fminf(fmaxf(c * inv, -MOE_E4M3_MAX), MOE_E4M3_MAX);
+    d = fminf(fmaxf(d * inv, -MOE_E4M3_MAX), MOE_E4M3_MAX);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// ---- wave-level reductions ------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, MOE_WAVE));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+    return v;
+}
+
+// max over aligned groups of 8 lanes
+__device__ __forceinline__ float group8_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1, MOE_WAVE));
+    v = fmaxf(v, __shfl_xor(v, 2, MOE_WAVE));
+    v = fmaxf(v, __shfl_xor(v, 4, MOE_WAVE));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+    return v;
+}
+
+// inclusive prefix sum across the wave
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int u = __shfl_up(v, o, MOE_WAVE);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Exclusive prefix sum of one int per thread over the whole block (blockDim.x a
+// multiple of 64, at most 1024). `scratch` holds >= 17 ints of LDS. Returns the
+// exclusive prefix; *total receives the block sum. Contains __syncthreads().
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int inc = wave_inclusive_scan(v, lane);
+    if (lane == 63) scratch[wid] = inc;
+    __syncthreads();
+    if (wid == 0) {
+        int w = lane < nw ? scratch[lane] : 0;
+        int wi = wave_inclusive_scan(w, lane);
+        if (lane < nw) scratch[lane] = wi - w;
+        if (lane == nw - 1) scratch[16] = wi;
+    }
+    __syncthreads();
+    int res = scratch[wid] + inc - v;
+    if (total) *total = scratch[16];
+    __syncthreads();
+    return res;
+}
+
+}  // namespace moe

@@ -1,0 +1,74 @@
+// Stage 5: top-k weighted combine of the expert outputs back to token order,
+// one wavefront per token.
+//
+// Follows "[1/2] sgl-kernel: Fuse routed scaling factor into select_experts"
+// (sglang PR #8364), Motivation: moe_sum_reduce is the weighted sum of each
+// token's selected expert outputs. The weights arrive from the gate with the
+// routed scaling factor already folded in (or not, as the caller chose); this
+// stage never applies it.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void post_reorder_kernel(const uint16_t* __restrict__ down,
+                                                           const int32_t* __restrict__ src2dst,
+                                                           const float* __restrict__ w, int64_t T,
+                                                           int H, int topk, int64_t m_cap,
+                                                           uint16_t* __restrict__ out) {
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wid;
+    if (t >= T) return;
+    int r = -1;
+    float wt = 0.0f;
+    if (lane < topk) {
+        const int32_t v = src2dst[t * topk + lane];
+        if (v >= 0 && v < m_cap) {
+            r = v;
+            wt = w[t * topk + lane];
+        }
+    }
+    const uint64_t mask = __ballot(r >= 0);
+    for (int c = lane * 8; c < H; c += 512) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        uint64_t m = mask;
+        while (m) {
+            const int j = __ffsll((unsigned long long)m) - 1;
+            m &= m - 1;
+            const int rj = __builtin_amdgcn_readlane(r, j);
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), j));
+            const uint4 v = *(const uint4*)(down + (int64_t)rj * H + c);
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = acc[2 * q] + wj * bf16_lo(d[q]);
+                acc[2 * q + 1] = acc[2 * q + 1] + wj * bf16_hi(d[q]);
+            }
+        }
+        uint4 o;
+        o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+        o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+        o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
+        o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
+        *(uint4*)(out + t * H + c) = o;
+    }
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_post_reorder(const void* down_bf16, const int32_t* src2dst,
+                                const float* topk_weights, int64_t T, int32_t H, int32_t topk,
+                                int64_t m_cap, void* out_bf16, void* stream) {
+    using namespace moe;
+    if (T < 0 || H <= 0 || topk <= 0 || m_cap < 0) return MOE_ERR_INVALID_ARG;
+    if (H % 16 != 0 || topk > 64) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!src2dst || !topk_weights || !out_bf16 || (m_cap > 0 && !down_bf16)) return MOE_ERR_NULL;
+    if ((down_bf16 && !aligned16(down_bf16)) || !aligned16(out_bf16)) return MOE_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(post_reorder_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
+                       (hipStream_t)stream, (const uint16_t*)down_bf16, src2dst, topk_weights, T,
+                       H, topk, m_cap, (uint16_t*)out_bf16);
+    return launch_status();
+}

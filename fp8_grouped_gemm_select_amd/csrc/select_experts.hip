@@ -1,0 +1,171 @@
+// Stage 1: the fused gate (scoring, grouped top-k, renormalisation, routed
+// scaling factor), one wavefront per token.
+//
+// Follows "[1/2] sgl-kernel: Fuse routed scaling factor into select_experts"
+// (sglang PR #8364), Motivation and Modifications: the scaling factor is
+// multiplied into the weights inside the gate, during the expert-weight
+// normalisation, when the boolean argument asks for it.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTokensPerBlock = 4;  // one wave per token, 256 threads
+
+// a ranks before b: larger key first, equal keys by lower index
+__device__ __forceinline__ bool ranks_before(float ka, int ia, float kb, int ib) {
+    return ka > kb || (ka == kb && ia < ib);
+}
+
+// Each lane owns EPL consecutive experts: e = lane*EPL + i.
+template <int EPL>
+__global__ __launch_bounds__(256) void select_experts_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int E, int topk,
+    int n_group, int topk_group, int score_fn, int renormalize, float rsf, int apply_rsf,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+    __shared__ float s_key[kTokensPerBlock][EPL * 64];
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kTokensPerBlock + wid;
+    const bool active = t < T;  // waves stay for the block barriers below
+    const float* l = logits + (active ? t : 0) * E;
+
+    float key[EPL], sc[EPL];
+    bool ok[EPL];
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane * EPL + i;
+        ok[i] = active && e < E;
+        const float lv = ok[i] ? l[e] : 0.0f;
+        if (score_fn == MOE_SCORE_SIGMOID) {
+            sc[i] = sigmoid_fixed(lv);
+            key[i] = bias ? sc[i] + (ok[i] ? bias[e] : 0.0f) : sc[i];
+        } else {
+            sc[i] = lv;
+            key[i] = lv;
+            if (ok[i]) lmax = fmaxf(lmax, lv);
+        }
+    }
+
+    // ---- group-limited selection ----
+    if (n_group > 1) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) s_key[wid][lane * EPL + i] = key[i];
+        __syncthreads();
+        const int gs = E / n_group;
+        float gscore = -INFINITY;
+        if (lane < n_group) {
+            float k1 = -INFINITY, k2 = -INFINITY;
+            int i1 = 0x7fffffff, i2 = 0x7fffffff;
+            for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
+                const float v = s_key[wid][e];
+                if (ranks_before(v, e, k1, i1)) { k2 = k1; i2 = i1; k1 = v; i1 = e; }
+                else if (ranks_before(v, e, k2, i2)) { k2 = v; i2 = e; }
+            }
+            gscore = gs >= 2 ? k1 + k2 : k1;
+        }
+        uint64_t keep = 0;
+        bool taken_g = false;
+        for (int r = 0; r < topk_group; ++r) {
+            float bk = (lane < n_group && !taken_g) ? gscore : -INFINITY;
+            int bi = (lane < n_group && !taken_g) ? lane : 0x7fffffff;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const float ok2 = __shfl_xor(bk, o, MOE_WAVE);
+                const int oi = __shfl_xor(bi, o, MOE_WAVE);
+                if (ranks_before(ok2, oi, bk, bi)) { bk = ok2; bi = oi; }
+            }
+            keep |= 1ull << bi;
+            if (lane == bi) taken_g = true;
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane * EPL + i;
+            if (ok[i] && !((keep >> (e / gs)) & 1ull)) ok[i] = false;
+        }
+    }
+
+    // ---- top-k over the allowed experts ----
+    int my_id = 0;
+    float my_sc = 0.0f;
+    for (int j = 0; j < topk; ++j) {
+        float bk = -INFINITY, bs = 0.0f;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane * EPL + i;
+            if (ok[i] && ranks_before(key[i], e, bk, bi)) { bk = key[i]; bi = e; bs = sc[i]; }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ok2 = __shfl_xor(bk, o, MOE_WAVE);
+            const int oi = __shfl_xor(bi, o, MOE_WAVE);
+            const float os = __shfl_xor(bs, o, MOE_WAVE);
+            if (ranks_before(ok2, oi, bk, bi)) { bk = ok2; bi = oi; bs = os; }
+        }
+        if (lane == j) { my_id = bi; my_sc = bs; }
+        if (bi / EPL == lane) {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (lane * EPL + i == bi) ok[i] = false;
+        }
+    }
+
+    // ---- weights ----
+    float v = 0.0f;
+    float all = 1.0f;
+    if (score_fn == MOE_SCORE_SOFTMAX) {
+        const float m = wave_max(lmax);
+        if (lane < topk) v = exp_fixed(my_sc - m);
+        if (!renormalize) {
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (active && lane * EPL + i < E) part += exp_fixed(sc[i] - m);
+            all = wave_sum(part);
+        }
+    } else if (lane < topk) {
+        v = my_sc;
+    }
+    const float sel = wave_sum(lane < topk ? v : 0.0f);
+    float w = v / (renormalize ? sel : all);
+    if (apply_rsf) w = w * rsf;
+    if (active && lane < topk) {
+        ids_out[t * topk + lane] = my_id;
+        w_out[t * topk + lane] = w;
+    }
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_select_experts(const float* logits, const float* correction_bias, int64_t T,
+                                  int32_t E, int32_t topk, int32_t n_group, int32_t topk_group,
+                                  int32_t score_fn, int32_t renormalize,
+                                  float routed_scaling_factor, int32_t apply_rsf,
+                                  int32_t* topk_ids, float* topk_weights, void* stream) {
+    using namespace moe;
+    if (T < 0 || E <= 0 || topk <= 0 || n_group <= 0 || topk_group <= 0) return MOE_ERR_INVALID_ARG;
+    if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+    if (E > 512 || topk > 32 || topk > E || n_group > 64) return MOE_ERR_UNSUPPORTED;
+    if (E % n_group != 0 || topk_group > n_group) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)topk_group * (E / n_group) < topk) return MOE_ERR_INVALID_ARG;
+    if (score_fn == MOE_SCORE_SOFTMAX && (correction_bias || n_group > 1)) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+    if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_weights))
+        return MOE_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    const dim3 grid((unsigned)ceil_div(T, kTokensPerBlock)), block(256);
+    hipStream_t s = (hipStream_t)stream;
+#define MOE_LAUNCH_SELECT(EPL)                                                                     \
+    hipLaunchKernelGGL(select_experts_kernel<EPL>, grid, block, 0, s, logits, correction_bias, T, \
+                       E, topk, n_group, topk_group, score_fn, renormalize,                      \
+                       routed_scaling_factor, apply_rsf, topk_ids, topk_weights)
+    if (E <= 64) MOE_LAUNCH_SELECT(1);
+    else if (E <= 128) MOE_LAUNCH_SELECT(2);
+    else if (E <= 256) MOE_LAUNCH_SELECT(4);
+    else MOE_LAUNCH_SELECT(8);
+#undef MOE_LAUNCH_SELECT
+    return launch_status();
+}

@@ -1,0 +1,84 @@
+"""One EP-MoE layer forward on one GPU: the five libmoe stages in order.
+
+Buffers are allocated once (``LayerBuffers``) with torch, sized for the worst
+case (m_cap = T * min(topk, num_local) local rows), and reused by every call;
+``layer_forward`` only enqueues the five C-ABI calls on the current stream and
+never synchronises. The data-dependent row count M stays on the device in
+``seg_indptr[num_local]``.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import (moe_act_requant, moe_grouped_gemm_fp8, moe_post_reorder, moe_pre_reorder_quant,
+               moe_select_experts, moe_workspace_bytes, ACT_PER_GROUP, ACT_PER_TENSOR,
+               ACT_PER_TOKEN)
+
+
+def _scale_numel(act_quant: int, m_cap: int, K: int) -> int:
+    if act_quant == ACT_PER_TENSOR:
+        return 1
+    if act_quant == ACT_PER_TOKEN:
+        return m_cap
+    return m_cap * (-(-K // 128))
+
+
+@dataclasses.dataclass
+class LayerBuffers:
+    topk_ids: torch.Tensor
+    topk_weights: torch.Tensor
+    src2dst: torch.Tensor
+    dst2src: torch.Tensor
+    seg_indptr: torch.Tensor
+    a13: torch.Tensor
+    a13_scale: torch.Tensor
+    c13: torch.Tensor
+    a2: torch.Tensor
+    a2_scale: torch.Tensor
+    c2: torch.Tensor
+    out: torch.Tensor
+    workspace: torch.Tensor
+
+    @staticmethod
+    def allocate(T, H, I, topk, num_local, act_quant, device="cuda"):
+        m_cap = T * min(topk, num_local)
+        dev = torch.device(device)
+        ws = moe_workspace_bytes(T, topk, num_local)
+        return LayerBuffers(
+            topk_ids=torch.empty((T, topk), dtype=torch.int32, device=dev),
+            topk_weights=torch.empty((T, topk), dtype=torch.float32, device=dev),
+            src2dst=torch.empty(T * topk, dtype=torch.int32, device=dev),
+            dst2src=torch.empty(m_cap, dtype=torch.int32, device=dev),
+            seg_indptr=torch.empty(num_local + 1, dtype=torch.int32, device=dev),
+            a13=torch.empty((m_cap, H), dtype=torch.uint8, device=dev),
+            a13_scale=torch.empty(_scale_numel(act_quant, m_cap, H), dtype=torch.float32, device=dev),
+            c13=torch.empty((m_cap, 2 * I), dtype=torch.bfloat16, device=dev),
+            a2=torch.empty((m_cap, I), dtype=torch.uint8, device=dev),
+            a2_scale=torch.empty(_scale_numel(act_quant, m_cap, I), dtype=torch.float32, device=dev),
+            c2=torch.empty((m_cap, H), dtype=torch.bfloat16, device=dev),
+            out=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+            workspace=torch.empty(max(ws, 256), dtype=torch.uint8, device=dev),
+        )
+
+
+def layer_forward(x, logits, correction_bias, w13, w13_scale, w2, w2_scale, buf: LayerBuffers, *,
+                  topk, n_group, topk_group, score_fn, renormalize, routed_scaling_factor,
+                  apply_rsf, expert_start, num_local, act_quant, w_quant, stream=None):
+    """x bf16 [T,H], logits fp32 [T,E]; w13 e4m3 [E_l,2I,H]; w2 e4m3 [E_l,H,I]. Result in buf.out."""
+    moe_select_experts(logits, correction_bias, buf.topk_ids, buf.topk_weights, topk=topk,
+                       n_group=n_group, topk_group=topk_group, score_fn=score_fn,
+                       renormalize=renormalize, routed_scaling_factor=routed_scaling_factor,
+                       apply_rsf=apply_rsf, stream=stream)
+    moe_pre_reorder_quant(x, buf.topk_ids, buf.a13, buf.a13_scale, buf.src2dst, buf.dst2src,
+                          buf.seg_indptr, buf.workspace, expert_start=expert_start,
+                          num_local=num_local, act_quant=act_quant, stream=stream)
+    moe_grouped_gemm_fp8(buf.a13, buf.a13_scale, w13, w13_scale, buf.seg_indptr, buf.c13,
+                         act_quant=act_quant, w_quant=w_quant, stream=stream)
+    moe_act_requant(buf.c13, buf.seg_indptr, buf.a2, buf.a2_scale, buf.workspace,
+                    act_quant=act_quant, stream=stream)
+    moe_grouped_gemm_fp8(buf.a2, buf.a2_scale, w2, w2_scale, buf.seg_indptr, buf.c2,
+                         act_quant=act_quant, w_quant=w_quant, stream=stream)
+    moe_post_reorder(buf.c2, buf.src2dst, buf.topk_weights, buf.out, stream=stream)
+    return buf.out

@@ -57,6 +57,8 @@ def _load():
     lib.oracle_pre_reorder_quant.argtypes = [P, P, I64, I32, I32, I32, P, P]
     lib.oracle_grouped_gemm.restype = ctypes.c_int
     lib.oracle_grouped_gemm.argtypes = [P, P, I32, P, P, I32, P, I32, I32, I32, P, I32]
+    lib.oracle_grouped_gemm_rows.restype = ctypes.c_int
+    lib.oracle_grouped_gemm_rows.argtypes = [P, P, I32, P, P, I32, P, I32, I32, I32, P, I64, P]
     lib.oracle_act_requant.restype = ctypes.c_int
     lib.oracle_act_requant.argtypes = [P, P, I32, I32, I32, P, P]
     lib.oracle_post_reorder.restype = ctypes.c_int
@@ -187,6 +189,25 @@ def grouped_gemm(a_q, a_scale, act_quant, b_q, b_scale, w_quant, seg_indptr, fla
     rc = _load().oracle_grouped_gemm(_p(a_q), _p(a_scale), act_quant, _p(b_q), _p(b_scale),
                                      w_quant, _p(seg), num_local, N, K, _p(c), flags)
     _check(rc, "grouped_gemm")
+    return c
+
+
+def grouped_gemm_rows(a_q, a_scale, act_quant, b_q, b_scale, w_quant, seg_indptr, rows):
+    """Stage 3 for selected rows only: returns bf16 bits [len(rows), N]."""
+    a_q = _c(a_q, np.uint8)
+    b_q = _c(b_q, np.uint8)
+    a_scale = _c(a_scale, np.float32)
+    b_scale = _c(b_scale, np.float32)
+    seg = _c(seg_indptr, np.int32)
+    rows = _c(rows, np.int64)
+    K = a_q.shape[1]
+    num_local, N, K2 = b_q.shape
+    assert K == K2
+    c = np.zeros((len(rows), N), dtype=np.uint16)
+    rc = _load().oracle_grouped_gemm_rows(_p(a_q), _p(a_scale), act_quant, _p(b_q), _p(b_scale),
+                                          w_quant, _p(seg), num_local, N, K, _p(rows), len(rows),
+                                          _p(c))
+    _check(rc, "grouped_gemm_rows")
     return c
 
 

@@ -451,6 +451,36 @@ int oracle_grouped_gemm(const uint8_t* a_q, const float* a_scale, int act_quant,
     return 0;
 }
 
+/* Selected output rows only (for sampled checks at full size): c_rows[i, :] =
+ * C[rows[i], :] of oracle_grouped_gemm. Rows outside every segment give zeros. */
+int oracle_grouped_gemm_rows(const uint8_t* a_q, const float* a_scale, int act_quant,
+                             const uint8_t* b_q, const float* b_scale, int w_quant,
+                             const int32_t* seg_indptr, int num_local, int N, int K,
+                             const int64_t* rows, int64_t nrows, uint16_t* c_rows) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t r = rows[i];
+        int e = -1;
+        for (int q = 0; q < num_local; ++q)
+            if (r >= seg_indptr[q] && r < seg_indptr[q + 1]) e = q;
+        uint16_t* out = c_rows + i * N;
+        if (e < 0) { memset(out, 0, sizeof(uint16_t) * (size_t)N); continue; }
+        float* ahat = (float*)malloc(sizeof(float) * K);
+        float* bhat = (float*)malloc(sizeof(float) * (size_t)K);
+        dequant_a_row(a_q, a_scale, act_quant, r, r, K, ahat);
+        int KB = (K + QB - 1) / QB;
+        for (int n = 0; n < N; ++n) {
+            for (int k = 0; k < K; ++k)
+                bhat[k] = oracle_e4m3_decode(b_q[((int64_t)e * N + n) * K + k])
+                          * b_scale_at(b_scale, w_quant, e, n, k / QB, N, KB);
+            gemm_row(ahat, bhat, 1, K, out + n);
+        }
+        free(ahat);
+        free(bhat);
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------- */
 /* (4) SiLU-and-mul + dynamic requantisation                                  */
 /* ------------------------------------------------------------------------- */

@@ -1,0 +1,350 @@
+"""Stage-isolated GPU parity: each libmoe stage against the CPU oracle on the
+same seeded inputs, through the C ABI.
+
+Bit-exact: expert ids, src2dst / dst2src / seg_indptr, FP8 codes and scales.
+Within tolerance: routing weights (4e-6 relative), GEMM outputs (the layer
+tolerance, atol 1e-2 + rtol 2e-2, and exact in the exact-arithmetic case),
+combine (one bf16 ulp of the fp64 sum).
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["tiny", "dsv3_decode_ep", "dsv3_prefill_ep", "mixtral", "skewed_block"]
+
+
+@functools.lru_cache(maxsize=2)
+def routed(name, seed=0):
+    """Token bits, logits/bias and the oracle's routing for a named workload."""
+    cfg = W.CONFIGS[name]
+    inp = W.gen_layer_inputs(cfg, seed=seed, weights=False)
+    ids, w = oracle.select_experts(inp.logits, inp.bias, cfg.topk, cfg.n_group, cfg.topk_group,
+                                   cfg.score_fn, cfg.renormalize, cfg.rsf, cfg.apply_rsf)
+    return cfg, inp, ids, w
+
+
+def check_weights(w, ref):
+    assert np.all(np.abs(w.astype(np.float64) - ref) <= 4e-6 * np.abs(ref) + 1e-12)
+
+
+# ---- stage 1 ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", FULL)
+def test_select_experts_workloads(name):
+    cfg, inp, ids_ref, w_ref = routed(name)
+    print(f"select_experts {name} T={cfg.T} E={cfg.E}", flush=True)
+    ids, w = G.run_select(inp.logits, inp.bias, cfg.topk, cfg.n_group, cfg.topk_group,
+                          cfg.score_fn, cfg.renormalize, cfg.rsf, cfg.apply_rsf)
+    assert np.array_equal(ids, ids_ref)
+    check_weights(w, w_ref)
+
+
+@pytest.mark.parametrize("case", ["ties_softmax", "ties_sigmoid_grouped", "k_eq_e", "no_renorm",
+                                  "no_rsf", "odd_T", "E512", "one_token"])
+def test_select_experts_edges(case):
+    g = np.random.default_rng(11)
+    kw = dict(topk=2, n_group=1, topk_group=1, score_fn=W.SCORE_SOFTMAX, renormalize=1, rsf=1.0,
+              apply_rsf=1)
+    bias = None
+    if case == "ties_softmax":
+        logits = g.integers(-2, 3, (37, 16)).astype(np.float32)
+        kw.update(topk=5)
+    elif case == "ties_sigmoid_grouped":
+        logits = g.integers(-1, 2, (37, 64)).astype(np.float32)
+        bias = np.zeros(64, np.float32)
+        kw.update(topk=6, n_group=8, topk_group=3, score_fn=W.SCORE_SIGMOID, rsf=2.5)
+    elif case == "k_eq_e":
+        logits = g.standard_normal((33, 8)).astype(np.float32)
+        kw.update(topk=8)
+    elif case == "no_renorm":
+        logits = g.standard_normal((40, 128)).astype(np.float32)
+        kw.update(topk=8, renormalize=0)
+    elif case == "no_rsf":
+        logits = g.standard_normal((40, 256)).astype(np.float32) * 2
+        bias = (g.standard_normal(256) * 0.01).astype(np.float32)
+        kw.update(topk=8, n_group=8, topk_group=4, score_fn=W.SCORE_SIGMOID, rsf=2.5, apply_rsf=0)
+    elif case == "odd_T":
+        logits = g.standard_normal((5, 256)).astype(np.float32)
+        bias = (g.standard_normal(256) * 0.01).astype(np.float32)
+        kw.update(topk=8, n_group=8, topk_group=4, score_fn=W.SCORE_SIGMOID, rsf=2.5)
+    elif case == "E512":
+        logits = g.standard_normal((9, 512)).astype(np.float32)
+        kw.update(topk=32)
+    else:
+        logits = g.standard_normal((1, 32)).astype(np.float32)
+        bias = (g.standard_normal(32) * 0.1).astype(np.float32)
+        kw.update(topk=4, n_group=4, topk_group=2, score_fn=W.SCORE_SIGMOID, renormalize=0)
+    print(f"select_experts edge {case}", flush=True)
+    ids_ref, w_ref = oracle.select_experts(logits, bias, kw["topk"], kw["n_group"], kw["topk_group"],
+                                           kw["score_fn"], kw["renormalize"], kw["rsf"], kw["apply_rsf"])
+    ids, w = G.run_select(logits, bias, **kw)
+    assert np.array_equal(ids, ids_ref)
+    check_weights(w, w_ref)
+
+
+# ---- stage 2 ----------------------------------------------------------------------
+
+def check_pre(res, ref_perm, ref_q, act_quant, H):
+    s2d, d2s, seg = ref_perm
+    a_q_ref, a_s_ref = ref_q
+    assert np.array_equal(res["seg"], seg)
+    assert np.array_equal(res["src2dst"], s2d)
+    assert np.array_equal(res["dst2src"], d2s)
+    M = int(seg[-1])
+    assert np.array_equal(res["a_q"][:M], a_q_ref[:M])
+    if act_quant == W.ACT_PER_TENSOR:
+        assert res["a_scale"][0].view(np.uint32) == a_s_ref[0].view(np.uint32)
+    else:
+        Gq = 1 if act_quant == W.ACT_PER_TOKEN else -(-H // 128)
+        assert np.array_equal(res["a_scale"][:M * Gq].view(np.uint32), a_s_ref[:M * Gq].view(np.uint32))
+
+
+def pre_case(x_bits, ids, expert_start, num_local, act_quant):
+    T, H = x_bits.shape
+    topk = ids.shape[1]
+    m_cap = T * min(topk, num_local)
+    ref_perm = oracle.permute(ids, expert_start, num_local, m_cap)
+    ref_q = oracle.pre_reorder_quant(x_bits, ref_perm[0], topk, act_quant, m_cap)
+    res = G.run_pre(x_bits, ids, expert_start, num_local, act_quant)
+    check_pre(res, ref_perm, ref_q, act_quant, H)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_pre_reorder_workloads(name):
+    cfg, inp, ids, _ = routed(name)
+    print(f"pre_reorder {name} T={cfg.T} H={cfg.H}", flush=True)
+    pre_case(inp.x, ids, cfg.expert_start, cfg.num_local, cfg.act_quant)
+
+
+@pytest.mark.parametrize("act_quant", [W.ACT_PER_TENSOR, W.ACT_PER_TOKEN, W.ACT_PER_GROUP])
+@pytest.mark.parametrize("shape", [(1, 16, 4, 2, 0, 8), (63, 144, 16, 4, 3, 5), (65, 9216, 8, 8, 0, 8),
+                                   (200, 256, 64, 6, 10, 20), (130, 384, 8, 2, 0, 1)])
+def test_pre_reorder_ragged(act_quant, shape):
+    T, H, E, topk, start, nl = shape
+    g = np.random.default_rng(T * 7 + H)
+    x = g.standard_normal((T, H)).astype(np.float32) * (2.0 ** (np.arange(T) % 9 - 4))[:, None]
+    x[T // 2] = 0.0
+    ids = np.stack([g.permutation(E)[:topk] for _ in range(T)]).astype(np.int32)
+    print(f"pre_reorder ragged T={T} H={H} E={E} k={topk} local=[{start},{start + nl}) mode={act_quant}",
+          flush=True)
+    pre_case(W.to_bf16_bits(x.astype(np.float32)), ids, start, nl, act_quant)
+
+
+def test_pre_reorder_no_local_and_empty():
+    g = np.random.default_rng(3)
+    x = W.to_bf16_bits(g.standard_normal((40, 64)).astype(np.float32))
+    ids = np.stack([g.permutation(16)[:4] for _ in range(40)]).astype(np.int32)
+    print("pre_reorder no local experts", flush=True)
+    res = G.run_pre(x, ids, 16, 4, W.ACT_PER_TOKEN)       # experts 16..19 do not occur
+    assert np.all(res["seg"] == 0) and np.all(res["src2dst"] == -1) and np.all(res["dst2src"] == -1)
+    print("pre_reorder zero local experts", flush=True)
+    res = G.run_pre(x, ids, 0, 0, W.ACT_PER_TOKEN)
+    assert np.all(res["seg"] == 0) and np.all(res["src2dst"] == -1)
+
+
+def test_e4m3_encoder_on_device_matches_oracle():
+    """Rows whose |max| is 448 have scale 1: the codes are the e4m3 rounding of the
+    bf16 values themselves, covering every e4m3 midpoint and its bf16 neighbours."""
+    table = oracle.e4m3_decode_table().astype(np.float64)
+    pos = table[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    vals = []
+    for m in mids:
+        b = int(W.to_bf16_bits(np.array([m], np.float32))[0])
+        vals += [b - 1, b, b + 1]
+    vals = np.array(vals, dtype=np.uint16)
+    vals = np.concatenate([vals, vals | 0x8000, W.to_bf16_bits(pos.astype(np.float32)),
+                           np.array([0x0000, 0x8000, 0x0001, 0x8001], np.uint16)])
+    H = 256
+    n = -(-len(vals) // (H - 1))
+    rows = np.zeros((n, H), dtype=np.uint16)
+    flat = np.zeros(n * (H - 1), dtype=np.uint16)
+    flat[:len(vals)] = vals
+    rows[:, :H - 1] = flat.reshape(n, H - 1)
+    rows[:, H - 1] = W.to_bf16_bits(np.array([448.0], np.float32))[0]
+    ids = np.zeros((n, 1), np.int32)
+    print(f"e4m3 encoder rows={n}", flush=True)
+    res = G.run_pre(rows, ids, 0, 1, W.ACT_PER_TOKEN)
+    assert np.all(res["a_scale"][:n] == 1.0)
+    expect = np.array([[oracle.e4m3_encode(float(v)) for v in W.bf16_bits_to_f32(r)] for r in rows],
+                      dtype=np.uint8)
+    assert np.array_equal(res["a_q"][:n], expect)
+
+
+# ---- stage 3 ------------------------------------------------------------------------
+
+from tests.test_oracle_layer import _exact_gemm_case  # noqa: E402
+
+
+@pytest.mark.parametrize("act_quant,w_quant", [(W.ACT_PER_TENSOR, W.W_PER_EXPERT),
+                                               (W.ACT_PER_TOKEN, W.W_PER_EXPERT),
+                                               (W.ACT_PER_TOKEN, W.W_PER_CHANNEL),
+                                               (W.ACT_PER_GROUP, W.W_BLOCK),
+                                               (W.ACT_PER_GROUP, W.W_PER_CHANNEL),
+                                               (W.ACT_PER_TOKEN, W.W_BLOCK)])
+def test_grouped_gemm_exact_case(act_quant, w_quant):
+    a_q, sa, b_q, sb, seg, expect, m_cap = _exact_gemm_case(act_quant, w_quant)
+    print(f"grouped_gemm exact act={act_quant} w={w_quant}", flush=True)
+    c = G.run_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg)
+    M = seg[-1]
+    assert np.array_equal(c[:M], expect[:M])
+
+
+def _rand_gemm(seed, counts, N, K, act_quant, w_quant, extra=7):
+    g = np.random.default_rng(seed)
+    counts = np.asarray(counts)
+    E_l = len(counts)
+    seg = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    m_cap = int(seg[-1]) + extra
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    a_q = finite[g.integers(0, len(finite), (m_cap, K))]
+    b_q = finite[g.integers(0, len(finite), (E_l, N, K))]
+    na = W.a_scale_numel(act_quant, m_cap, K)
+    nb = W.b_scale_numel(w_quant, E_l, N, K)
+    sa = g.uniform(1e-3, 4e-3, na).astype(np.float32)
+    sb = g.uniform(1e-4, 4e-4, nb).astype(np.float32)
+    return a_q, sa, b_q, sb, seg
+
+
+def abs_products(a_q, sa, act_quant, b_q, sb, w_quant, seg, rows):
+    """sum_k |a_hat[r,k] * b_hat[e,n,k]| for the given rows (fp64), the scale of the
+    fp32 summation error of either side."""
+    table = np.abs(oracle.e4m3_decode_table().astype(np.float64))
+    m_cap, K = a_q.shape
+    E_l, N, _ = b_q.shape
+    KB, NB = -(-K // 128), -(-N // 128)
+    out = np.zeros((len(rows), N))
+    for i, r in enumerate(rows):
+        e = int(np.searchsorted(seg, r, side="right") - 1)
+        if act_quant == W.ACT_PER_TENSOR:
+            sa_row = np.full(K, sa[0], np.float64)
+        elif act_quant == W.ACT_PER_TOKEN:
+            sa_row = np.full(K, sa[r], np.float64)
+        else:
+            sa_row = np.repeat(sa[r * KB:(r + 1) * KB].astype(np.float64), 128)[:K]
+        a = table[a_q[r]] * np.abs(sa_row)
+        bt = table[b_q[e]]
+        if w_quant == W.W_PER_EXPERT:
+            bt = bt * abs(float(sb[e]))
+        elif w_quant == W.W_PER_CHANNEL:
+            bt = bt * np.abs(sb[e * N:(e + 1) * N].astype(np.float64))[:, None]
+        else:
+            blk = np.abs(sb[e * NB * KB:(e + 1) * NB * KB].astype(np.float64)).reshape(NB, KB)
+            bt = bt * np.repeat(np.repeat(blk, 128, 0), 128, 1)[:N, :K]
+        out[i] = bt @ a
+    return out
+
+
+@pytest.mark.parametrize("act_quant,w_quant", [(W.ACT_PER_TENSOR, W.W_PER_EXPERT),
+                                               (W.ACT_PER_TOKEN, W.W_PER_CHANNEL),
+                                               (W.ACT_PER_GROUP, W.W_BLOCK)])
+@pytest.mark.parametrize("dims", [((37, 0, 300, 5, 129), 256, 512), ((1,), 128, 128),
+                                  ((17, 40), 48, 80), ((0, 260, 3), 384, 1024)])
+def test_grouped_gemm_random(act_quant, w_quant, dims):
+    counts, N, K = dims
+    if w_quant == W.W_BLOCK and (N % 128 or K % 128):
+        N, K = 128 * -(-N // 128), 128 * -(-K // 128)
+    a_q, sa, b_q, sb, seg = _rand_gemm(5, counts, N, K, act_quant, w_quant)
+    print(f"grouped_gemm random counts={counts} N={N} K={K} act={act_quant} w={w_quant}", flush=True)
+    ref = oracle.grouped_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg)
+    c = G.run_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg)
+    M = seg[-1]
+    G.assert_close_layer(c[:M], ref[:M], what="C")
+    rows = np.arange(M)
+    G.assert_sum_close(c[:M], ref[:M], abs_products(a_q, sa, act_quant, b_q, sb, w_quant, seg, rows),
+                       K, what="C")
+
+
+@pytest.mark.parametrize("name,which", [("dsv3_prefill_ep", "w13"), ("dsv3_prefill_ep", "w2"),
+                                        ("mixtral", "w13"), ("skewed_block", "w2"),
+                                        ("dsv3_decode_ep", "w13")])
+def test_grouped_gemm_full_size_sampled_rows(name, which):
+    """Full workload shapes in the benchmark's launch configuration; 48 sampled rows
+    (all N columns) recomputed by the oracle one row at a time."""
+    cfg, inp, ids, _ = routed(name)
+    m_cap = cfg.m_cap
+    s2d, d2s, seg = oracle.permute(ids, cfg.expert_start, cfg.num_local, m_cap)
+    M = int(seg[-1])
+    g = np.random.default_rng(1)
+    if which == "w13":
+        K, N = cfg.H, 2 * cfg.I
+        a_q, sa = oracle.pre_reorder_quant(inp.x, s2d, cfg.topk, cfg.act_quant, m_cap)
+    else:
+        K, N = cfg.I, cfg.H
+        a_q = g.integers(0, 0x7E, (m_cap, K)).astype(np.uint8) | (g.integers(0, 2, (m_cap, K)) * 0x80).astype(np.uint8)
+        sa = g.uniform(1e-3, 4e-3, W.a_scale_numel(cfg.act_quant, m_cap, K)).astype(np.float32)
+    b_q, sb = W.gen_weights(cfg, which)
+    print(f"grouped_gemm full {name} {which} M={M} N={N} K={K}", flush=True)
+    c = G.run_gemm(a_q, sa, cfg.act_quant, b_q, sb, cfg.w_quant, seg)
+    rows = np.unique(np.concatenate([g.integers(0, M, 44), [0, M - 1], seg[1:-1][:2]]))
+    rows = rows[rows < M]
+    ref = oracle.grouped_gemm_rows(a_q, sa, cfg.act_quant, b_q, sb, cfg.w_quant, seg, rows)
+    G.assert_close_layer(c[rows], ref, what="C rows")
+    G.assert_sum_close(c[rows], ref, abs_products(a_q, sa, cfg.act_quant, b_q, sb, cfg.w_quant, seg,
+                                                  rows), K, what="C rows")
+
+
+# ---- stage 4 ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("act_quant", [W.ACT_PER_TENSOR, W.ACT_PER_TOKEN, W.ACT_PER_GROUP])
+@pytest.mark.parametrize("dims", [((20, 0, 31), 64), ((300, 17), 2048), ((5,), 9216), ((64, 64), 768)])
+def test_act_requant_ragged(act_quant, dims):
+    counts, I = dims
+    g = np.random.default_rng(len(counts) * 100 + I)
+    seg = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    m_cap = int(seg[-1]) + 9
+    gu = W.to_bf16_bits((g.standard_normal((m_cap, 2 * I)) * 1.7).astype(np.float32))
+    print(f"act_requant counts={counts} I={I} mode={act_quant}", flush=True)
+    a_ref, s_ref = oracle.act_requant(gu, seg, act_quant)
+    a_q, a_s = G.run_act(gu, seg, act_quant)
+    M = int(seg[-1])
+    assert np.array_equal(a_q[:M], a_ref[:M])
+    Gq = 1 if act_quant == W.ACT_PER_TOKEN else -(-I // 128)
+    n = 1 if act_quant == W.ACT_PER_TENSOR else M * Gq
+    assert np.array_equal(a_s[:n].view(np.uint32), s_ref[:n].view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["dsv3_prefill_ep", "mixtral", "skewed_block"])
+def test_act_requant_full_size(name):
+    cfg, inp, ids, _ = routed(name)
+    s2d, d2s, seg = oracle.permute(ids, cfg.expert_start, cfg.num_local, cfg.m_cap)
+    g = np.random.default_rng(2)
+    gu = W.to_bf16_bits((g.standard_normal((cfg.m_cap, 2 * cfg.I), dtype=np.float32) * np.float32(1.7)))
+    print(f"act_requant full {name} M={seg[-1]} I={cfg.I}", flush=True)
+    a_ref, s_ref = oracle.act_requant(gu, seg, cfg.act_quant)
+    a_q, a_s = G.run_act(gu, seg, cfg.act_quant)
+    M = int(seg[-1])
+    assert np.array_equal(a_q[:M], a_ref[:M])
+    Gq = 1 if cfg.act_quant == W.ACT_PER_TOKEN else -(-cfg.I // 128)
+    n = 1 if cfg.act_quant == W.ACT_PER_TENSOR else M * Gq
+    assert np.array_equal(a_s[:n].view(np.uint32), s_ref[:n].view(np.uint32))
+
+
+# ---- stage 5 ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "dsv3_prefill_ep", "skewed_block"])
+def test_post_reorder(name):
+    cfg, inp, ids, w = routed(name)
+    s2d, d2s, seg = oracle.permute(ids, cfg.expert_start, cfg.num_local, cfg.m_cap)
+    g = np.random.default_rng(4)
+    down = W.to_bf16_bits(g.standard_normal((cfg.m_cap, cfg.H), dtype=np.float32))
+    print(f"post_reorder {name} T={cfg.T} H={cfg.H}", flush=True)
+    ref = oracle.post_reorder(down, s2d, w, cfg.T, cfg.topk)
+    out = G.run_post(down, s2d, w, cfg.T, cfg.topk)
+    d = np.abs(G.bf16_to_f64(down))
+    sd = s2d.reshape(cfg.T, cfg.topk)
+    abs_terms = np.zeros((cfg.T, cfg.H))
+    for j in range(cfg.topk):
+        ok = sd[:, j] >= 0
+        abs_terms[ok] += np.abs(w[ok, j].astype(np.float64))[:, None] * d[sd[ok, j]]
+    G.assert_sum_close(out, ref, abs_terms, cfg.topk, what="combine")
+    none = np.all(s2d.reshape(cfg.T, cfg.topk) < 0, axis=1)
+    assert np.all(out[none] == 0)

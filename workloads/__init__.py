@@ -18,6 +18,7 @@ with tensor_id 0 = tokens X, 1 = router weights W_g, 2 = correction bias,
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
@@ -227,13 +228,15 @@ def gen_expert_weight(cfg: MoEConfig, which: str, e_local: int, seed: int = 0):
 
 
 def gen_weights(cfg: MoEConfig, which: str, seed: int = 0):
-    """All local experts' codes [E_l, N, K] uint8 and scales fp32 (mode-shaped, flattened per expert)."""
-    codes, scales = [], []
-    for e in range(cfg.num_local):
-        c, s = gen_expert_weight(cfg, which, e, seed)
-        codes.append(c)
-        scales.append(s.reshape(-1))
-    return np.stack(codes), np.stack(scales)
+    """All local experts' codes [E_l, N, K] uint8 and scales fp32 (mode-shaped, flattened per expert).
+
+    Experts are drawn in parallel threads; each has its own generator, so the
+    result does not depend on the thread count."""
+    import concurrent.futures as cf
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        parts = list(ex.map(lambda e: gen_expert_weight(cfg, which, e, seed), range(cfg.num_local)))
+    return np.stack([c for c, _ in parts]), np.stack([s.reshape(-1) for _, s in parts])
 
 
 @dataclasses.dataclass
