@@ -158,13 +158,15 @@ def assert_within_bf16_ulps(got_bits, ref_bits, ulps=1, what="output"):
 
 
 def assert_sum_close(got_bits, ref_bits, abs_terms, n_terms, what="output", ulps=1):
-    """|got - ref| <= `ulps` bf16 ulps of ref + two fp32 summation error bounds
-    (n_terms * 2^-24 * sum|terms|, one for each side's accumulation order).
+    """|got - ref| <= `ulps` bf16 ulps of ref + fp32 summation error bounds of both
+    sides: n_terms * 2^-24 * sum|terms| for the oracle's round-to-nearest sum, and
+    n_terms * 2^-23 * sum|terms| for the GPU, whose matrix-core accumulation order
+    and rounding inside one instruction are not specified.
     abs_terms is the sum of the absolute values of the summed products."""
     g = bf16_to_f64(got_bits)
     r = bf16_to_f64(ref_bits)
     ulp = np.maximum(np.abs(r), 2.0 ** -126) * 2.0 ** -7
-    bound = ulps * ulp * (1 + 1e-9) + 2.0 * n_terms * 2.0 ** -24 * abs_terms
+    bound = ulps * ulp * (1 + 1e-9) + 3.0 * n_terms * 2.0 ** -24 * abs_terms
     err = np.abs(g - r)
     bad = err > bound
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} values outside the bound; "

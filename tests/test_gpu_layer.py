@@ -3,8 +3,8 @@ the CPU oracle on the same seeded inputs.
 
 Ids and permutation bit-exact; the bf16 layer output within atol 1e-2 + rtol
 2e-2. Small ragged layers are compared in full; the full-size workloads on
-sampled tokens recomputed by the oracle's dense per-token loop. Also: two runs
-are bitwise identical, and experts with no tokens are never read.
+sampled tokens, which the oracle recomputes as a batch of their own. Also: two
+runs are bitwise identical, and experts with no tokens are never read.
 """
 import dataclasses
 
@@ -100,9 +100,18 @@ def test_layer_rsf_scales_output_once():
 
 @pytest.mark.parametrize("name", ["dsv3_decode_ep", "dsv3_prefill_ep", "skewed_block"])
 def test_layer_full_size_sampled_tokens(name):
-    """Full workload in the benchmark's launch configuration: routing and
-    permutation compared in full, the output on 24 sampled tokens recomputed by
-    the dense per-token oracle."""
+    """Full workload in the benchmark's launch configuration. Routing and
+    permutation are compared in full. For sampled tokens (all of them at decode)
+    the oracle runs the permuted layer on just those tokens (every step is
+    token-local in these per-token / per-group modes), and the GPU's w13 output
+    rows, w2-input scales and layer output are compared with it.
+
+    The GEMM accumulation order legitimately moves a w13 output by one bf16
+    step; when that step lands on a row's maximum, the row's requantisation
+    scale moves by one bf16 step of amax and every code of the row is re-rounded
+    against it -- a different, equally valid FP8 encoding. Tokens without such a
+    row must meet atol 1e-2 + rtol 2e-2; tokens with one must stay within that
+    tolerance plus one e4m3 step on every requantised value of the moved row."""
     cfg = W.CONFIGS[name]
     inp = W.gen_layer_inputs(cfg, seed=0)
     print(f"layer full {name} T={cfg.T}", flush=True)
@@ -110,18 +119,80 @@ def test_layer_full_size_sampled_tokens(name):
     ids_ref, w_ref = oracle.select_experts(inp.logits, inp.bias, cfg.topk, cfg.n_group,
                                            cfg.topk_group, cfg.score_fn, cfg.renormalize,
                                            cfg.rsf, cfg.apply_rsf)
-    ids = buf.topk_ids.cpu().numpy()
-    assert np.array_equal(ids, ids_ref)
+    assert np.array_equal(buf.topk_ids.cpu().numpy(), ids_ref)
     s2d, d2s, seg = oracle.permute(ids_ref, cfg.expert_start, cfg.num_local, cfg.m_cap)
     assert np.array_equal(buf.seg_indptr.cpu().numpy(), seg)
-    assert np.array_equal(buf.src2dst.cpu().numpy(), s2d)
+    gpu_s2d = buf.src2dst.cpu().numpy()
+    assert np.array_equal(gpu_s2d, s2d)
+    w_gpu = buf.topk_weights.cpu().numpy()
+    assert np.all(np.abs(w_gpu.astype(np.float64) - w_ref) <= 4e-6 * np.abs(w_ref))
+
     g = np.random.default_rng(5)
-    local_tok = np.nonzero(np.any(s2d.reshape(cfg.T, cfg.topk) >= 0, axis=1))[0]
-    toks = np.unique(np.concatenate([g.choice(local_tok, 20, replace=False), [0, cfg.T - 1]]))
-    w = buf.topk_weights.cpu().numpy()
-    ref = oracle.dense_layer(inp.x[toks], ids_ref[toks], w_ref[toks], cfg.I, cfg.expert_start,
-                             cfg.num_local, cfg.act_quant, inp.w13, inp.w13_scale, inp.w2,
-                             inp.w2_scale, cfg.w_quant)
-    out = G.bf16_bits(buf.out)[toks]
-    G.assert_close_layer(out, ref, what=f"{name} sampled tokens")
-    assert np.all(np.abs(w[toks].astype(np.float64) - w_ref[toks]) <= 4e-6 * np.abs(w_ref[toks]))
+    if cfg.T <= 256:
+        toks = np.arange(cfg.T)
+    else:
+        local_tok = np.nonzero(np.any(s2d.reshape(cfg.T, cfg.topk) >= 0, axis=1))[0]
+        toks = np.unique(np.concatenate([g.choice(local_tok, 40, replace=False), [0, cfg.T - 1]]))
+    sub = dataclasses.replace(inp, cfg=dataclasses.replace(cfg, T=len(toks)), x=inp.x[toks],
+                              logits=inp.logits[toks])
+    ref = oracle.layer(sub)
+    k = cfg.topk
+    r_gpu = gpu_s2d.reshape(cfg.T, k)[toks]
+    r_ref = ref["src2dst"].reshape(len(toks), k)
+    assert np.array_equal(r_gpu >= 0, r_ref >= 0)
+
+    c13 = G.bf16_bits(buf.c13)
+    a2s = buf.a2_scale.cpu().numpy()
+    Gq = 1 if cfg.act_quant == W.ACT_PER_TOKEN else -(-cfg.I // 128)
+    table = np.abs(oracle.e4m3_decode_table().astype(np.float64))
+    out_gpu = G.bf16_to_f64(G.bf16_bits(buf.out)[toks])
+    out_ref = G.bf16_to_f64(ref["out"])
+    extra = np.zeros_like(out_ref)
+    moved_rows = 0
+    for i in range(len(toks)):
+        for j in range(k):
+            if r_ref[i, j] < 0:
+                continue
+            rg, rr = int(r_gpu[i, j]), int(r_ref[i, j])
+            e = int(ids_ref[toks[i], j]) - cfg.expert_start
+            # w13 output row: the GEMM bound
+            a13_abs = table[ref["a13"][rr]] * np.repeat(
+                np.abs(ref["a13_scale"][rr * (1 if Gq == 1 else -(-cfg.H // 128)):][
+                    :(1 if Gq == 1 else -(-cfg.H // 128))]).astype(np.float64),
+                128 if Gq != 1 else cfg.H)[:cfg.H]
+            b13 = np.asarray(inp.w13_scale[e]).reshape(-1).astype(np.float64)
+            if cfg.w_quant == W.W_PER_CHANNEL:
+                b13_abs = table[inp.w13[e]] * np.abs(b13)[:, None]
+            else:
+                nb, kb = -(-2 * cfg.I // 128), -(-cfg.H // 128)
+                b13_abs = table[inp.w13[e]] * np.repeat(np.repeat(np.abs(b13).reshape(nb, kb), 128, 0),
+                                                          128, 1)[:2 * cfg.I, :cfg.H]
+            G.assert_sum_close(c13[rg], ref["c13"][rr], b13_abs @ a13_abs, cfg.H,
+                               what=f"{name} w13 row of token {toks[i]} slot {j}")
+            sg = a2s[rg * Gq:(rg + 1) * Gq].astype(np.float64)
+            sr = ref["a2_scale"][rr * Gq:(rr + 1) * Gq].astype(np.float64)
+            if np.array_equal(sg, sr):
+                continue
+            # a moved requantisation scale must be one bf16 step of amax away, at most
+            assert np.all(np.abs(sg - sr) <= sr * 2.0 ** -7 * (1 + 1e-6)), (toks[i], j)
+            moved_rows += 1
+            h_abs = table[ref["a2"][rr]] * np.repeat(sr, 128 if Gq != 1 else cfg.I)[:cfg.I] * (1 + 2.0 ** -4)
+            b2 = np.asarray(inp.w2_scale[e]).reshape(-1).astype(np.float64)
+            if cfg.w_quant == W.W_PER_CHANNEL:
+                b2_abs = table[inp.w2[e]] * np.abs(b2)[:, None]
+            else:
+                nb, kb = -(-cfg.H // 128), -(-cfg.I // 128)
+                b2_abs = table[inp.w2[e]] * np.repeat(np.repeat(np.abs(b2).reshape(nb, kb), 128, 0),
+                                                        128, 1)[:cfg.H, :cfg.I]
+            # one e4m3 step per value: 2^-3 relative in the normal range, 2^-9 * scale
+            # absolute among subnormals, plus the scale's own one-step move
+            s_full = np.repeat(sr, 128 if Gq != 1 else cfg.I)[:cfg.I]
+            step = h_abs * (2.0 ** -3 + 2.0 ** -6) + 2.0 ** -9 * s_full
+            extra[i] += abs(float(w_ref[toks[i], j])) * (b2_abs @ step)
+    err = np.abs(out_gpu - out_ref)
+    tol = 1e-2 + 2e-2 * np.abs(out_ref)
+    strict = extra.max(axis=1) == 0
+    print(f"{name}: {len(toks)} tokens, {moved_rows} rows with a moved requantisation scale, "
+          f"worst |diff| {err.max():.4g}", flush=True)
+    assert np.all(err[strict] <= tol[strict]), "output outside atol 1e-2 + rtol 2e-2"
+    assert np.all(err <= tol + extra), "output outside the moved-scale bound"

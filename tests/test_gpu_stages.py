@@ -218,6 +218,8 @@ def abs_products(a_q, sa, act_quant, b_q, sb, w_quant, seg, rows):
     """sum_k |a_hat[r,k] * b_hat[e,n,k]| for the given rows (fp64), the scale of the
     fp32 summation error of either side."""
     table = np.abs(oracle.e4m3_decode_table().astype(np.float64))
+    sa = np.asarray(sa).reshape(-1)
+    sb = np.asarray(sb).reshape(-1)
     m_cap, K = a_q.shape
     E_l, N, _ = b_q.shape
     KB, NB = -(-K // 128), -(-N // 128)
