@@ -98,21 +98,31 @@ def test_layer_rsf_scales_output_once():
     assert np.all(np.abs(o25 - 2.5 * o1) <= np.abs(o25) * 2.0 ** -7 + 1e-30)
 
 
+def e4m3_ordinal(codes):
+    """Signed position of an e4m3 code on the number line (codes are sign-magnitude)."""
+    c = np.asarray(codes).astype(np.int32)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
 @pytest.mark.parametrize("name", ["dsv3_decode_ep", "dsv3_prefill_ep", "skewed_block"])
 def test_layer_full_size_sampled_tokens(name):
     """Full workload in the benchmark's launch configuration. Routing and
     permutation are compared in full. For sampled tokens (all of them at decode)
     the oracle runs the permuted layer on just those tokens (every step is
-    token-local in these per-token / per-group modes), and the GPU's w13 output
-    rows, w2-input scales and layer output are compared with it.
+    token-local in these per-token / per-group modes), and the GPU's w13 rows,
+    w2-input codes and scales, and layer output are compared with it.
 
-    The GEMM accumulation order legitimately moves a w13 output by one bf16
-    step; when that step lands on a row's maximum, the row's requantisation
-    scale moves by one bf16 step of amax and every code of the row is re-rounded
-    against it -- a different, equally valid FP8 encoding. Tokens without such a
-    row must meet atol 1e-2 + rtol 2e-2; tokens with one must stay within that
-    tolerance plus one e4m3 step on every requantised value of the moved row."""
+    The grouped GEMM's accumulation order legitimately moves a w13 output by a
+    bf16 step or more where the sum cancels. SiLU-and-mul and the FP8
+    requantisation can turn that into different e4m3 codes or a different row
+    scale: an equally valid encoding of slightly different inputs. So the w2
+    input is checked exactly against the oracle's stage 4 applied to the GPU's
+    own w13 rows, and the layer output must be within atol 1e-2 + rtol 2e-2 of
+    the oracle plus the exact propagated effect of the encoding differences,
+    sum_k |w2_hat[n,k]| * |h_gpu[k] - h_ref[k]| weighted by the routing weight
+    (zero where the encodings agree)."""
     cfg = W.CONFIGS[name]
+    assert cfg.act_quant != W.ACT_PER_TENSOR, "the sub-batch recomputation needs token-local scales"
     inp = W.gen_layer_inputs(cfg, seed=0)
     print(f"layer full {name} T={cfg.T}", flush=True)
     buf = run_layer(inp)
@@ -142,57 +152,54 @@ def test_layer_full_size_sampled_tokens(name):
     assert np.array_equal(r_gpu >= 0, r_ref >= 0)
 
     c13 = G.bf16_bits(buf.c13)
+    a2g_all = buf.a2.cpu().numpy()
     a2s = buf.a2_scale.cpu().numpy()
-    Gq = 1 if cfg.act_quant == W.ACT_PER_TOKEN else -(-cfg.I // 128)
-    table = np.abs(oracle.e4m3_decode_table().astype(np.float64))
+    G1 = 1 if cfg.act_quant == W.ACT_PER_TOKEN else -(-cfg.H // 128)
+    G2 = 1 if cfg.act_quant == W.ACT_PER_TOKEN else -(-cfg.I // 128)
+    table = oracle.e4m3_decode_table().astype(np.float64)
     out_gpu = G.bf16_to_f64(G.bf16_bits(buf.out)[toks])
     out_ref = G.bf16_to_f64(ref["out"])
     extra = np.zeros_like(out_ref)
-    moved_rows = 0
+    flips = total = moved = 0
+
+    def expand(scales, n):
+        return np.repeat(np.asarray(scales, np.float64), 128 if len(scales) > 1 else n)[:n]
+
+    def w_abs(which, e, N, K):
+        sc = np.abs(np.asarray(getattr(inp, which + "_scale")[e]).reshape(-1).astype(np.float64))
+        codes = np.abs(table[getattr(inp, which)[e]])
+        if cfg.w_quant == W.W_PER_CHANNEL:
+            return codes * sc[:, None]
+        nb, kb = -(-N // 128), -(-K // 128)
+        return codes * np.repeat(np.repeat(sc.reshape(nb, kb), 128, 0), 128, 1)[:N, :K]
+
     for i in range(len(toks)):
         for j in range(k):
             if r_ref[i, j] < 0:
                 continue
             rg, rr = int(r_gpu[i, j]), int(r_ref[i, j])
             e = int(ids_ref[toks[i], j]) - cfg.expert_start
-            # w13 output row: the GEMM bound
-            a13_abs = table[ref["a13"][rr]] * np.repeat(
-                np.abs(ref["a13_scale"][rr * (1 if Gq == 1 else -(-cfg.H // 128)):][
-                    :(1 if Gq == 1 else -(-cfg.H // 128))]).astype(np.float64),
-                128 if Gq != 1 else cfg.H)[:cfg.H]
-            b13 = np.asarray(inp.w13_scale[e]).reshape(-1).astype(np.float64)
-            if cfg.w_quant == W.W_PER_CHANNEL:
-                b13_abs = table[inp.w13[e]] * np.abs(b13)[:, None]
-            else:
-                nb, kb = -(-2 * cfg.I // 128), -(-cfg.H // 128)
-                b13_abs = table[inp.w13[e]] * np.repeat(np.repeat(np.abs(b13).reshape(nb, kb), 128, 0),
-                                                          128, 1)[:2 * cfg.I, :cfg.H]
-            G.assert_sum_close(c13[rg], ref["c13"][rr], b13_abs @ a13_abs, cfg.H,
-                               what=f"{name} w13 row of token {toks[i]} slot {j}")
-            sg = a2s[rg * Gq:(rg + 1) * Gq].astype(np.float64)
-            sr = ref["a2_scale"][rr * Gq:(rr + 1) * Gq].astype(np.float64)
-            if np.array_equal(sg, sr):
-                continue
-            # a moved requantisation scale must be one bf16 step of amax away, at most
-            assert np.all(np.abs(sg - sr) <= sr * 2.0 ** -7 * (1 + 1e-6)), (toks[i], j)
-            moved_rows += 1
-            h_abs = table[ref["a2"][rr]] * np.repeat(sr, 128 if Gq != 1 else cfg.I)[:cfg.I] * (1 + 2.0 ** -4)
-            b2 = np.asarray(inp.w2_scale[e]).reshape(-1).astype(np.float64)
-            if cfg.w_quant == W.W_PER_CHANNEL:
-                b2_abs = table[inp.w2[e]] * np.abs(b2)[:, None]
-            else:
-                nb, kb = -(-cfg.H // 128), -(-cfg.I // 128)
-                b2_abs = table[inp.w2[e]] * np.repeat(np.repeat(np.abs(b2).reshape(nb, kb), 128, 0),
-                                                        128, 1)[:cfg.H, :cfg.I]
-            # one e4m3 step per value: 2^-3 relative in the normal range, 2^-9 * scale
-            # absolute among subnormals, plus the scale's own one-step move
-            s_full = np.repeat(sr, 128 if Gq != 1 else cfg.I)[:cfg.I]
-            step = h_abs * (2.0 ** -3 + 2.0 ** -6) + 2.0 ** -9 * s_full
-            extra[i] += abs(float(w_ref[toks[i], j])) * (b2_abs @ step)
+            # w13 output row: one bf16 step plus the fp32 summation bounds
+            a13_abs = np.abs(table[ref["a13"][rr]]) * expand(np.abs(ref["a13_scale"][rr * G1:(rr + 1) * G1]), cfg.H)
+            G.assert_sum_close(c13[rg], ref["c13"][rr], w_abs("w13", e, 2 * cfg.I, cfg.H) @ a13_abs,
+                               cfg.H, what=f"{name} w13 row of token {toks[i]} slot {j}")
+            # w2 input: exactly the oracle's stage 4 of the GPU's own w13 row
+            q_own, s_own = oracle.act_requant(c13[rg:rg + 1], np.array([0, 1], np.int32), cfg.act_quant)
+            sg = a2s[rg * G2:(rg + 1) * G2].astype(np.float64)
+            sr = ref["a2_scale"][rr * G2:(rr + 1) * G2].astype(np.float64)
+            qg, qr = a2g_all[rg], ref["a2"][rr]
+            assert np.array_equal(qg, q_own[0]), (toks[i], j)
+            assert np.array_equal(a2s[rg * G2:(rg + 1) * G2].view(np.uint32), s_own[:G2].view(np.uint32)), (toks[i], j)
+            flips += int((qg != qr).sum())
+            total += cfg.I
+            moved += int((sg != sr).any())
+            dh = np.abs(table[qg] * expand(sg, cfg.I) - table[qr] * expand(sr, cfg.I))
+            if dh.any():
+                extra[i] += abs(float(w_ref[toks[i], j])) * (w_abs("w2", e, cfg.H, cfg.I) @ dh)
     err = np.abs(out_gpu - out_ref)
     tol = 1e-2 + 2e-2 * np.abs(out_ref)
-    strict = extra.max(axis=1) == 0
-    print(f"{name}: {len(toks)} tokens, {moved_rows} rows with a moved requantisation scale, "
-          f"worst |diff| {err.max():.4g}", flush=True)
-    assert np.all(err[strict] <= tol[strict]), "output outside atol 1e-2 + rtol 2e-2"
-    assert np.all(err <= tol + extra), "output outside the moved-scale bound"
+    print(f"{name}: {len(toks)} tokens, {flips} of {total} w2-input codes differ, {moved} rows "
+          f"with a moved scale, worst |diff| {err.max():.4g}, worst excess over tolerance "
+          f"{(err - tol).max():.3g}", flush=True)
+    assert flips <= 0.02 * total
+    assert np.all(err <= tol + extra), "output outside tolerance plus the propagated code differences"
