@@ -179,7 +179,7 @@ def main():
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = int(db)
     roof["algorithmic_flops"] = int(df)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(cfg.name, dom)
     gemm_t = (stage_ms["gemm_w13"] + stage_ms["gemm_w2"]) * 1e-3
     gemm_f = work["gemm_w13"]["flops"] + work["gemm_w2"]["flops"]
     gemm = dict(tflops=round(gemm_f / gemm_t / 1e12, 1),
@@ -215,6 +215,22 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary of this workload, or None when there is none or the
+    stage's kernel source has changed since the counters were taken."""
+    from fp8_grouped_gemm_select_amd import profsum
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    st = t.get("stages", {}).get(stage)
+    if not st or st.get("source_sha256") != profsum.source_hash(stage):
+        return None
+    return st["traffic_bytes"]
+
+
 def cpu_baseline(cfg, inp, sample_tokens):
     """The oracle, as it stands, on the first `sample_tokens` tokens of the same workload."""
     import dataclasses
@@ -223,7 +239,7 @@ def cpu_baseline(cfg, inp, sample_tokens):
     threads = len(os.sched_getaffinity(0))
     oracle.set_threads(threads)
     if not sample_tokens:
-        sample_tokens = {"tiny": 16, "dsv3_decode_ep": 128, "dsv3_prefill_ep": 512,
+        sample_tokens = {"tiny": 16, "dsv3_decode_ep": 128, "dsv3_prefill_ep": 1024,
                          "mixtral": 64, "skewed_block": 512}.get(cfg.name, 256)
     Ts = min(sample_tokens, cfg.T)
     sub = dataclasses.replace(inp, cfg=dataclasses.replace(cfg, T=Ts), x=inp.x[:Ts],
