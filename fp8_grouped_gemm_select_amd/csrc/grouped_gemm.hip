@@ -8,30 +8,34 @@
 // checks the activation scale's size for its mode.
 //
 // Design
-//   - Persistent grid (a multiple of 8 blocks, two per CU). Every block derives
-//     the tile list on the device from seg_indptr, so the host never learns M
-//     and nothing synchronises: a tile is (expert, n-tile, m-tile) in
-//     expert-major order with the m-tile fastest, so blocks running together
-//     share one expert's B columns and A rows through L2.
-//   - XCD-aware: workgroups are dealt to the 8 XCDs round robin, so block b
-//     (XCD b % 8) takes tiles from the XCD's own contiguous eighth of the list.
-//   - Tile 128 x 128 x 128 (BM x BN x BK), 256 threads = 4 waves in 2 x 2, each
-//     wave 64 x 64 = 4 x 4 MFMA 16x16x128 blocks. The MFMA is issued as B x A
-//     so that a lane's four accumulator values are four adjacent output columns
-//     of one row.
-//   - Operands are staged through two LDS buffers: the global loads of K step
-//     k+1 are in flight (in registers) while step k's MFMAs run, then written
-//     to the other buffer; one barrier per K step. LDS rows are 128 bytes =
-//     eight 16-byte chunks, chunk c of row r stored at c ^ perm8(r), which keeps
-//     both the row-wise stores and the MFMA operand reads (16 rows x one chunk
-//     per 16 lanes) free of bank conflicts on the 64-bank LDS.
-//   - Scales: when neither scale varies along K the fp32 accumulator is
-//     multiplied once by sa(row) * sb(e, n) in the epilogue. Otherwise every
-//     128-wide K step (exactly one MFMA deep) is accumulated separately and
-//     added with its factor sa(row, kb) * sb(e, n, kb).
-//   - Epilogue: each wave converts its 64 x 64 outputs to bf16 into LDS and
-//     writes them back as 16-byte row segments (eight rows of 128 bytes per
-//     store instruction).
+//   Two kernels share the tile schedule: a persistent grid in which every block
+//   derives the tile list on the device from seg_indptr (the host never learns
+//   M and nothing synchronises). A tile is (expert, n-tile, m-tile) in
+//   expert-major order with the m-tile fastest, so blocks running together
+//   share one expert's B columns and A rows through L2. Workgroups are dealt to
+//   the 8 XCDs round robin, so block b (XCD b % 8) takes tiles from its XCD's
+//   own contiguous eighth of the list.
+//
+//   grouped_gemm_dma_kernel (K % 128 == 0, every workload here): 128 x 256
+//   tiles, one 512-thread block per CU, operands straight from memory into a
+//   three-stage LDS ring by global_load_lds_dwordx4; see its own comment.
+//
+//   grouped_gemm_kernel (any K % 16 == 0): 128 x 128 x 128 tiles, two
+//   256-thread blocks per CU; loads staged through registers into two LDS
+//   buffers (step k+1 in flight while step k's MFMAs run), one barrier per K
+//   step, zero fill past K.
+//
+//   Both: waves own 64 x 64 outputs = 4 x 4 MFMA 16x16x128 blocks, issued as
+//   B x A so that a lane's four accumulator values are four adjacent output
+//   columns of one row. LDS rows are 128 bytes = eight 16-byte chunks, chunk c
+//   of row r stored at c ^ perm8(r), which keeps the row-wise fills and the
+//   MFMA operand reads (16 rows x one chunk per 16 lanes) free of bank
+//   conflicts on the 64-bank LDS. Scales: when neither scale varies along K the
+//   fp32 accumulator is multiplied once by sa(row) * sb(e, n) in the epilogue;
+//   otherwise every 128-wide K step (exactly one MFMA deep) is accumulated
+//   separately and added with its factor sa(row, kb) * sb(e, n, kb). Epilogue:
+//   each wave converts its 64 x 64 outputs to bf16 into LDS and writes them
+//   back as 16-byte row segments (eight rows of 128 bytes per store).
 #include "common.h"
 
 namespace moe {
@@ -70,6 +74,69 @@ __device__ __forceinline__ v8i lds_operand(const uint8_t* lds, int row, int lane
 // chunk q of row r at q ^ (r & 7).
 __device__ __forceinline__ int ep_off(int r, int q) { return r * 128 + ((q ^ (r & 7)) << 4); }
 
+// Tile table in LDS from seg_indptr (entries clamped to [0, m_cap]): s_seg[e]
+// = first row of expert e, s_tstart[e] = index of its first tile in the list
+// (experts in order, each with ceil(rows / TM) * ceil(N / TN) tiles). Returns the
+// number of tiles. All threads of the block take part.
+template <int TM, int TN>
+__device__ int build_tile_table(const int32_t* __restrict__ seg_in, int num_local, int64_t m_cap, int N,
+                                int* s_seg, int* s_tstart, int* scan_scratch) {
+    const int tid = threadIdx.x, nthreads = blockDim.x;
+    const int n_tiles = (N + TN - 1) / TN;
+    for (int e = tid; e <= num_local; e += nthreads) {
+        int64_t v = seg_in[e];
+        v = v < 0 ? 0 : (v > m_cap ? m_cap : v);
+        s_seg[e] = (int)v;
+    }
+    __syncthreads();
+    const int per = (num_local + nthreads - 1) / nthreads;
+    int my_tiles = 0;
+    for (int q = 0; q < per; ++q) {
+        const int e = tid * per + q;
+        if (e < num_local) {
+            const int rows = s_seg[e + 1] - s_seg[e];
+            my_tiles += rows > 0 ? ((rows + TM - 1) / TM) * n_tiles : 0;
+        }
+    }
+    int total = 0;
+    int run = block_exclusive_scan(my_tiles, scan_scratch, &total);
+    for (int q = 0; q < per; ++q) {
+        const int e = tid * per + q;
+        if (e < num_local) {
+            s_tstart[e] = run;
+            const int rows = s_seg[e + 1] - s_seg[e];
+            run += rows > 0 ? ((rows + TM - 1) / TM) * n_tiles : 0;
+        }
+    }
+    if (tid == 0) s_tstart[num_local] = total;
+    __syncthreads();
+    return total;
+}
+
+// Tile lt of the list: expert e (largest e with s_tstart[e] <= lt), its first
+// row row0 and row end, and the first output column n0.
+struct TileCoord {
+    int e, row0, row_end, n0;
+};
+template <int TM, int TN>
+__device__ __forceinline__ TileCoord tile_coord(int lt, const int* s_seg, const int* s_tstart, int num_local) {
+    int lo = 0, hi = num_local - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tstart[mid] <= lt) lo = mid; else hi = mid - 1;
+    }
+    TileCoord t;
+    t.e = lo;
+    const int seg0 = s_seg[lo], seg1 = s_seg[lo + 1];
+    const int mt_e = (seg1 - seg0 + TM - 1) / TM;
+    const int idx = lt - s_tstart[lo];
+    const int nt = idx / mt_e, mt = idx - nt * mt_e;
+    t.row0 = seg0 + mt * TM;
+    t.row_end = t.row0 + TM < seg1 ? t.row0 + TM : seg1;
+    t.n0 = nt * TN;
+    return t;
+}
+
 template <bool KDEP>
 __global__ __launch_bounds__(kThreads, kBlocksPerCU) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, int act_quant,
@@ -84,39 +151,11 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void grouped_gemm_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid >> 1, wn = wid & 1;
-    const int n_tiles = (N + BN - 1) / BN;
     const int KB = (K + MOE_QB - 1) / MOE_QB;
     const int NB = (N + MOE_QB - 1) / MOE_QB;
     const int nk = (K + BK - 1) / BK;
 
-    // ---- tile table from seg_indptr (clamped to [0, m_cap]) ----
-    for (int e = tid; e <= num_local; e += kThreads) {
-        int64_t v = seg_in[e];
-        v = v < 0 ? 0 : (v > m_cap ? m_cap : v);
-        s_seg[e] = (int)v;
-    }
-    __syncthreads();
-    const int per = (num_local + kThreads - 1) / kThreads;
-    int my_tiles = 0;
-    for (int q = 0; q < per; ++q) {
-        const int e = tid * per + q;
-        if (e < num_local) {
-            const int rows = s_seg[e + 1] - s_seg[e];
-            my_tiles += rows > 0 ? ((rows + BM - 1) / BM) * n_tiles : 0;
-        }
-    }
-    int total = 0;
-    int run = block_exclusive_scan(my_tiles, scan_scratch, &total);
-    for (int q = 0; q < per; ++q) {
-        const int e = tid * per + q;
-        if (e < num_local) {
-            s_tstart[e] = run;
-            const int rows = s_seg[e + 1] - s_seg[e];
-            run += rows > 0 ? ((rows + BM - 1) / BM) * n_tiles : 0;
-        }
-    }
-    if (tid == 0) s_tstart[num_local] = total;
-    __syncthreads();
+    const int total = build_tile_table<BM, BN>(seg_in, num_local, m_cap, N, s_seg, s_tstart, scan_scratch);
 
     // ---- this block's share of the tile list ----
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd_blocks = gridDim.x >> 3;
@@ -129,20 +168,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void grouped_gemm_kernel(
     const int lr = tid >> 3, lc = (tid & 7) * 16;
 
     for (int lt = lt_begin + slot; lt < lt_end; lt += per_xcd_blocks) {
-        // expert: largest e with s_tstart[e] <= lt
-        int lo = 0, hi = num_local - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_tstart[mid] <= lt) lo = mid; else hi = mid - 1;
-        }
-        const int e = lo;
-        const int seg0 = s_seg[e], seg1 = s_seg[e + 1];
-        const int mt_e = (seg1 - seg0 + BM - 1) / BM;
-        const int idx = lt - s_tstart[e];
-        const int nt = idx / mt_e, mt = idx - nt * mt_e;
-        const int row0 = seg0 + mt * BM;
-        const int row_end = row0 + BM < seg1 ? row0 + BM : seg1;
-        const int n0 = nt * BN;
+        const TileCoord tc = tile_coord<BM, BN>(lt, s_seg, s_tstart, num_local);
+        const int e = tc.e, row0 = tc.row0, row_end = tc.row_end, n0 = tc.n0;
         const bool group_act = KDEP && act_quant == MOE_ACT_PER_GROUP;
         const bool block_w = KDEP && w_quant == MOE_W_BLOCK;
 
@@ -254,6 +281,212 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void grouped_gemm_kernel(
     }
 }
 
+
+// ---- large-tile kernel: 128 x 256 tiles, 8 waves, LDS-DMA into a 3-stage ring ----
+//
+// One 512-thread block per CU (two waves per SIMD). Waves in 2 (M) x 4 (N),
+// each owns 64 x 64 outputs (4 x 4 MFMA 16x16x128). Operands go from memory to
+// LDS with global_load_lds_dwordx4 (no register staging): a stage holds the A
+// tile (128 rows) and the B tile (256 rows) of one 128-byte K step, in the same
+// perm8-swizzled row layout as above. The loads of step k+2 are issued at step
+// k; each wave waits only for its own loads of the step it is about to read,
+// then one barrier per step publishes the stage. Requires K % 128 == 0 (every
+// stage is whole; no zero fill). Rows past the valid range re-read the last
+// valid row, so every wave issues the same loads every step.
+constexpr int DBM = 128, DBN = 256, DBK = 128;
+constexpr int kDThreads = 512;
+constexpr int kDStages = 3;
+constexpr int kDStageA = DBM * DBK;             // 16 KB
+constexpr int kDStage = (DBM + DBN) * DBK;      // 48 KB
+constexpr int kDmaA = DBM * DBK / 1024 / 8;     // 1 KB DMA instructions per wave per stage: 2
+constexpr int kDmaB = DBN * DBK / 1024 / 8;     // 4
+constexpr int kDma = kDmaA + kDmaB;             // 6
+
+// One 16-byte global -> LDS DMA per lane: from base + voff (base wave-uniform
+// in SGPRs, voff a per-lane 32-bit offset) to LDS address lds_base + 16 * lane
+// (lds_base wave-uniform, in M0). Inline assembly so that the compiler inserts
+// no waits of its own around it; every wait on these loads is explicit.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_base)
+                 : "memory");
+}
+
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt left alone
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
+
+template <bool KDEP>
+__global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, int act_quant,
+    const uint8_t* __restrict__ B, const float* __restrict__ sb, int w_quant,
+    const int32_t* __restrict__ seg_in, int num_local, int64_t m_cap, int N, int K,
+    uint16_t* __restrict__ C) {
+    __shared__ __align__(16) uint8_t lds[kDStages * kDStage];
+    __shared__ int s_seg[kMaxLocal + 1];
+    __shared__ int s_tstart[kMaxLocal + 1];
+    __shared__ int scan_scratch[17];
+    __shared__ float s_sa[kDStages][DBM];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid >> 2, wn = wid & 3;
+    const int KB = K / MOE_QB;
+    const int NB = (N + MOE_QB - 1) / MOE_QB;
+    const int nk = K / DBK;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const void*)lds;
+
+    const int total = build_tile_table<DBM, DBN>(seg_in, num_local, m_cap, N, s_seg, s_tstart, scan_scratch);
+
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd_blocks = gridDim.x >> 3;
+    const int per_xcd = (total + 7) / 8;
+    const int lt_begin = xcd * per_xcd;
+    const int lt_end = lt_begin + per_xcd < total ? lt_begin + per_xcd : total;
+
+    for (int lt = lt_begin + slot; lt < lt_end; lt += per_xcd_blocks) {
+        const TileCoord tc = tile_coord<DBM, DBN>(lt, s_seg, s_tstart, num_local);
+        const int e = tc.e, row0 = tc.row0, row_end = tc.row_end, n0 = tc.n0;
+        const int a_rows = row_end - row0, b_rows = N - n0 < DBN ? N - n0 : DBN;
+        const bool group_act = KDEP && act_quant == MOE_ACT_PER_GROUP;
+        const bool block_w = KDEP && w_quant == MOE_W_BLOCK;
+        // the weight-scale block of this wave's 64 columns (clamped: in a partial
+        // tile a wave's columns can start past N; its outputs are not stored)
+        const int nb_w = (n0 + wn * 64) / MOE_QB < NB ? (n0 + wn * 64) / MOE_QB : NB - 1;
+
+        // per-lane DMA offsets: instruction i of this wave fills LDS rows
+        // 8 * (wave's first block + i) + lane / 8, chunk position lane % 8, which
+        // holds global chunk (lane % 8) ^ perm8(row)
+        uint32_t a_off[kDmaA], b_off[kDmaB];
+#pragma unroll
+        for (int i = 0; i < kDmaA; ++i) {
+            const int r = (wid * kDmaA + i) * 8 + (lane >> 3);
+            const int g = r < a_rows ? r : a_rows - 1;
+            a_off[i] = (uint32_t)g * (uint32_t)K + (uint32_t)((((lane & 7) ^ perm8(r)) << 4));
+        }
+#pragma unroll
+        for (int i = 0; i < kDmaB; ++i) {
+            const int r = (wid * kDmaB + i) * 8 + (lane >> 3);
+            const int g = r < b_rows ? r : b_rows - 1;
+            b_off[i] = (uint32_t)g * (uint32_t)K + (uint32_t)((((lane & 7) ^ perm8(r)) << 4));
+        }
+        const uint8_t* a_g = A + (int64_t)row0 * K;
+        const uint8_t* b_g = B + ((int64_t)e * N + n0) * K;
+        const int sa_row = row0 + ((tid & (DBM - 1)) < a_rows ? (tid & (DBM - 1)) : a_rows - 1);
+
+        auto issue = [&](int k) {  // DMA of K step k into stage k % 3
+            const uint32_t st = lds0 + (uint32_t)((k % kDStages) * kDStage);
+            const uint8_t* ab = uniform_ptr(a_g + k * DBK);
+            const uint8_t* bb = uniform_ptr(b_g + k * DBK);
+            const uint32_t la = __builtin_amdgcn_readfirstlane(st + wid * kDmaA * 1024);
+            const uint32_t lb = __builtin_amdgcn_readfirstlane(st + kDStageA + wid * kDmaB * 1024);
+#pragma unroll
+            for (int i = 0; i < kDmaA; ++i) dma16(ab, a_off[i], la + i * 1024);
+#pragma unroll
+            for (int i = 0; i < kDmaB; ++i) dma16(bb, b_off[i], lb + i * 1024);
+        };
+
+        v4f acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+        // Issue order per step j: [activation group scales of step j+1] [DMA of
+        // step j+2]. At step k the wave needs DMA(k) (issued at step k-2) and
+        // the scales of step k (issued at step k-1); only DMA(k+1) was issued
+        // after them, so vmcnt(kDma) suffices while k + 1 < nk.
+        float q = 0.f;
+        if (group_act) q = sa[(int64_t)sa_row * KB];
+        issue(0);
+        if (nk > 1) issue(1);
+        for (int k = 0; k < nk; ++k) {
+            if (k + 1 < nk) wait_vmcnt<kDma>();
+            else wait_vmcnt<0>();
+            if (group_act && tid < DBM) s_sa[k % kDStages][tid] = q;
+            __syncthreads();  // stage k complete; every wave is done with stage k-1
+            if (group_act && k + 1 < nk) q = sa[(int64_t)sa_row * KB + k + 1];
+            if (k + 2 < nk) issue(k + 2);
+
+            const uint8_t* la = lds + (k % kDStages) * kDStage;
+            const uint8_t* lb = la + kDStageA;
+            v8i af[4], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = lds_operand(la, wm * 64 + i * 16 + (lane & 15), lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bfr[j] = lds_operand(lb, wn * 64 + j * 16 + (lane & 15), lane);
+
+            if (!KDEP) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bfr[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+            } else {
+                const float sbv = block_w ? sb[((int64_t)e * NB + nb_w) * KB + k] : 1.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float f = (group_act ? s_sa[k % kDStages][wm * 64 + i * 16 + (lane & 15)] : 1.0f) * sbv;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bfr[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[i][j][v] = acc[i][j][v] + t[v] * f;
+                    }
+                }
+            }
+        }
+        __syncthreads();  // every wave is done with the operand stages
+
+        // ---- epilogue: remaining scales, bf16 into LDS, 16-byte row stores ----
+        uint8_t* ep = lds + wid * (64 * 128);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rl = i * 16 + (lane & 15);
+            const int r = row0 + wm * 64 + rl;
+            float srow = 1.0f;
+            if (!group_act) srow = act_quant == MOE_ACT_PER_TENSOR ? sa[0] : sa[r < row_end ? r : row0];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int cl = j * 16 + (lane >> 4) * 4;
+                uint32_t h[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float scol = 1.0f;
+                    if (!block_w) {
+                        const int n = n0 + wn * 64 + cl + v;
+                        scol = w_quant == MOE_W_PER_EXPERT ? sb[e] : sb[(int64_t)e * N + (n < N ? n : N - 1)];
+                    }
+                    h[v] = f32_to_bf16_bits(acc[i][j][v] * (srow * scol));
+                }
+                *(uint2*)(ep + ep_off(rl, cl >> 3) + (cl & 7) * 2) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            }
+        }
+        __syncthreads();  // the staged blocks are complete (lanes read other lanes' values)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int rl = t * 8 + (lane >> 3), qc = lane & 7;
+            const int r = row0 + wm * 64 + rl;
+            const int n = n0 + wn * 64 + qc * 8;
+            const uint4 v = *(const uint4*)(ep + ep_off(rl, qc));
+            if (r < row_end && n < N) *(uint4*)(C + (int64_t)r * N + n) = v;
+        }
+        __syncthreads();  // the LDS is free for the next tile's stages
+    }
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -280,6 +513,23 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a_q, const float* a_scale, in
     if (!aligned16(a_q) || !aligned16(b_q) || !aligned16(c_bf16)) return MOE_ERR_INVALID_ARG;
 
     (void)hipGetLastError();
+    if (K % DBK == 0 && (int64_t)K * DBN < ((int64_t)1 << 32)) {
+        // large tiles, LDS-DMA pipeline: one block per CU
+        const int64_t upper = (ceil_div(m_cap, DBM) + num_local) * ceil_div(N, DBN);
+        int64_t g = (int64_t)device_cu_count();
+        if (g > ceil_div(upper, 8) * 8) g = ceil_div(upper, 8) * 8;
+        g = ceil_div(g < 8 ? 8 : g, 8) * 8;
+        hipStream_t st = (hipStream_t)stream;
+        if (act_quant == MOE_ACT_PER_GROUP || w_quant == MOE_W_BLOCK)
+            hipLaunchKernelGGL(grouped_gemm_dma_kernel<true>, dim3((unsigned)g), dim3(kDThreads), 0, st,
+                               a_q, a_scale, act_quant, b_q, b_scale, w_quant, seg_indptr, num_local,
+                               m_cap, N, K, (uint16_t*)c_bf16);
+        else
+            hipLaunchKernelGGL(grouped_gemm_dma_kernel<false>, dim3((unsigned)g), dim3(kDThreads), 0, st,
+                               a_q, a_scale, act_quant, b_q, b_scale, w_quant, seg_indptr, num_local,
+                               m_cap, N, K, (uint16_t*)c_bf16);
+        return launch_status();
+    }
     const int64_t upper_tiles = (ceil_div(m_cap, BM) + num_local) * ceil_div(N, BN);
     int64_t grid = (int64_t)device_cu_count() * kBlocksPerCU;
     if (grid > ceil_div(upper_tiles, 8) * 8) grid = ceil_div(upper_tiles, 8) * 8;
