@@ -3,7 +3,7 @@
 
 namespace moe {
 
-size_t pre_reorder_ws_bytes(int64_t T, int32_t num_local);
+size_t pre_reorder_ws_bytes(int64_t T, int32_t topk, int32_t num_local);
 size_t act_requant_ws_bytes();
 
 int device_cu_count() {
@@ -21,10 +21,10 @@ int device_cu_count() {
 }  // namespace moe
 
 extern "C" size_t moe_workspace_bytes(int64_t T, int32_t topk, int32_t num_local) {
-    (void)topk;
     if (T < 0) T = 0;
+    if (topk < 1) topk = 1;
     if (num_local < 0) num_local = 0;
-    const size_t a = moe::pre_reorder_ws_bytes(T, num_local);
+    const size_t a = moe::pre_reorder_ws_bytes(T, topk, num_local);
     const size_t b = moe::act_requant_ws_bytes();
     return a > b ? a : b;
 }

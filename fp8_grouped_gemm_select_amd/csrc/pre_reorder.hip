@@ -6,50 +6,61 @@
 // give per-token scales, and the scales travel with the rows through src2dst.
 // Here the scale reorder is fused into the scatter.
 //
-// A deterministic stable counting sort in three launches (plus one amax pass in
-// the per-tensor mode):
-//   count    one wave per chunk of kChunkTok tokens: chunk-local stable rank of
-//            every local pair (kept in src2dst) and per-expert chunk counts;
-//   scan     one block: per-expert exclusive scan over chunks, then over
-//            experts -> seg_indptr; per-tensor amax partials -> one scale;
-//   scatter  one wave per token: final rows, dst2src, and the quantised row
-//            written to each of the token's local rows.
+// A deterministic stable counting sort over the (token, slot) pairs
+// f = t * topk + slot, in chunks of 64 consecutive pairs (one wave each):
+//   count    a pair's stable rank among the chunk's earlier pairs of the same
+//            local expert (register compares, kept in src2dst) and the
+//            chunk's count per expert, stored expert-major [E_l][nchunks];
+//   scan     one block: a flat exclusive scan of those counts in expert-major
+//            order, so entry (e, c) is the first row of expert e's pairs from
+//            chunk c, and entry (e, 0) is seg_indptr[e]; per-tensor amax
+//            partials -> one scale;
+//   scatter  one wave per token: its row loads are issued as soon as its ids
+//            are known; final rows, dst2src, and the quantised row written to
+//            each of the token's local rows; the grid clears dst2src[M..m_cap).
 #include "common.h"
 
 namespace moe {
 namespace {
 
-constexpr int kChunkTok = 64;
+constexpr int kChunkPairs = 64;
 constexpr int kRegIters = 8;   // rows up to 8192 wide stay in registers
 constexpr int kAmaxBlocks = 1024;
 
 struct PreWs {
-    int32_t* counts;   // [nchunks][num_local]
-    int32_t* offs;     // [nchunks][num_local]
+    int32_t* counts;   // [num_local][nchunks]
+    int32_t* offs;     // [num_local][nchunks], exclusive scan of counts
     float* amax_part;  // [kAmaxBlocks]
     float* tscale;     // [2]: per-tensor scale, inverse
 };
 
 __host__ __device__ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-inline size_t pre_ws_bytes(int64_t T, int32_t num_local) {
-    const int64_t nch = ceil_div(T, kChunkTok);
+inline int64_t n_chunks(int64_t T, int32_t topk) { return ceil_div(T * (int64_t)topk, kChunkPairs); }
+
+// counts / offs entries, padded so that the scan's 16-byte loads stay inside
+inline int64_t n_entries(int64_t T, int32_t topk, int32_t num_local) {
+    return (n_chunks(T, topk) * num_local + 31) / 32 * 32 + 32;
+}
+
+inline size_t pre_ws_bytes(int64_t T, int32_t topk, int32_t num_local) {
+    const int64_t ne = n_entries(T, topk, num_local);
     size_t b = 0;
-    b += align256(sizeof(int32_t) * (size_t)(nch * num_local));
-    b += align256(sizeof(int32_t) * (size_t)(nch * num_local));
+    b += align256(sizeof(int32_t) * (size_t)ne);
+    b += align256(sizeof(int32_t) * (size_t)ne);
     b += align256(sizeof(float) * kAmaxBlocks);
     b += align256(sizeof(float) * 2);
     return b;
 }
 
-inline PreWs pre_ws_carve(void* ws, int64_t T, int32_t num_local) {
-    const int64_t nch = ceil_div(T, kChunkTok);
+inline PreWs pre_ws_carve(void* ws, int64_t T, int32_t topk, int32_t num_local) {
+    const int64_t ne = n_entries(T, topk, num_local);
     char* p = (char*)ws;
     PreWs w;
     w.counts = (int32_t*)p;
-    p += align256(sizeof(int32_t) * (size_t)(nch * num_local));
+    p += align256(sizeof(int32_t) * (size_t)ne);
     w.offs = (int32_t*)p;
-    p += align256(sizeof(int32_t) * (size_t)(nch * num_local));
+    p += align256(sizeof(int32_t) * (size_t)ne);
     w.amax_part = (float*)p;
     p += align256(sizeof(float) * kAmaxBlocks);
     w.tscale = (float*)p;
@@ -57,44 +68,36 @@ inline PreWs pre_ws_carve(void* ws, int64_t T, int32_t num_local) {
 }
 
 // ---- count: chunk-local stable ranks -----------------------------------------
-__global__ __launch_bounds__(64) void pr_count_kernel(const int32_t* __restrict__ ids, int64_t T,
-                                                      int topk, int expert_start, int num_local,
+// One 64-thread block per chunk of 64 pairs; lane l holds pair 64 c + l. Its
+// rank is the number of lower lanes holding the same local expert (compared
+// against every lane's expert via readlane); the lane holding an expert's last
+// occurrence in the chunk records the count. cnt[] (dynamic LDS, num_local
+// ints) gives every (expert, chunk) entry exactly one writer.
+__global__ __launch_bounds__(64) void pr_count_kernel(const int32_t* __restrict__ ids, int64_t F,
+                                                      int expert_start, int num_local, int64_t nch,
                                                       int32_t* __restrict__ src2dst,
                                                       int32_t* __restrict__ counts) {
     extern __shared__ int32_t cnt[];
     const int lane = threadIdx.x;
     const int64_t chunk = blockIdx.x;
     for (int e = lane; e < num_local; e += 64) cnt[e] = 0;
-    __syncthreads();
-    const int64_t f0 = chunk * kChunkTok * topk;
-    const int64_t t1 = (chunk + 1) * kChunkTok < T ? (chunk + 1) * kChunkTok : T;
-    const int64_t f1 = t1 * topk;
-    for (int64_t base = f0; base < f1; base += 64) {
-        const int64_t f = base + lane;
-        const int e = f < f1 ? ids[f] - expert_start : -1;
-        const bool local = e >= 0 && e < num_local;
-        bool pending = local;
-        int rank = -1;
-        // Resolve one expert value per round: lanes holding it take consecutive
-        // ranks in lane (= pair) order after the chunk's running count.
-        while (true) {
-            const uint64_t m = __ballot(pending);
-            if (m == 0) break;
-            const int leader = __ffsll((unsigned long long)m) - 1;
-            const int v = __shfl(e, leader, MOE_WAVE);
-            const uint64_t same = __ballot(pending && e == v);
-            const int base_cnt = cnt[v];
-            if (pending && e == v) {
-                rank = base_cnt + __popcll(same & lanemask_lt(lane));
-                pending = false;
-            }
-            if (lane == leader) cnt[v] = base_cnt + __popcll(same);
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // LDS write done before the next read
-        }
-        if (f < f1) src2dst[f] = local ? rank : -1;
+    const int64_t f = chunk * kChunkPairs + lane;
+    const int ev = f < F ? ids[f] - expert_start : -1;
+    const bool local = ev >= 0 && ev < num_local;
+    const int e = local ? ev : -1;
+    int below = 0, all = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        const bool m = ej == e;
+        below += (m && j < lane) ? 1 : 0;
+        all += m ? 1 : 0;
     }
+    __syncthreads();  // cnt[] cleared
+    if (local && below == all - 1) cnt[e] = all;
+    if (f < F) src2dst[f] = local ? below : -1;
     __syncthreads();
-    for (int e = lane; e < num_local; e += 64) counts[chunk * num_local + e] = cnt[e];
+    for (int x = lane; x < num_local; x += 64) counts[(int64_t)x * nch + chunk] = cnt[x];
 }
 
 // ---- per-tensor amax partials over all of x ---------------------------------------
@@ -114,9 +117,14 @@ __global__ __launch_bounds__(256) void pr_amax_kernel(const uint4* __restrict__ 
     if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// ---- scan: segment starts and per-chunk offsets ------------------------------------
+// ---- scan: flat exclusive scan of the expert-major counts ---------------------------
+// 1024 threads, in passes of 1024 x 32 entries: thread t loads its 32 contiguous
+// entries of the pass at once (8 x 16 bytes), the block scans the thread sums,
+// and the running carry joins the passes. The workspace rows are padded to a
+// multiple of 32 entries past n (zero counts), so the vector loads stay inside.
+constexpr int kScanPer = 32;
 __global__ __launch_bounds__(1024) void pr_scan_kernel(const int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ offs, int64_t nchunks,
+                                                       int32_t* __restrict__ offs, int64_t nch,
                                                        int num_local, int32_t* __restrict__ seg,
                                                        const float* __restrict__ amax_part,
                                                        int n_part, int per_tensor,
@@ -125,43 +133,46 @@ __global__ __launch_bounds__(1024) void pr_scan_kernel(const int32_t* __restrict
     __shared__ int scratch[17];
     __shared__ float red[16];
     const int tid = threadIdx.x;
-    // experts handled by this thread: a contiguous run
-    const int per = (num_local + 1023) / 1024;
-    const int e0 = tid * per;
-    int mine = 0;
-    for (int q = 0; q < per; ++q) {
-        const int e = e0 + q;
-        if (e >= num_local) break;
-        int run = 0;
-        int64_t c = 0;
-        for (; c + 8 <= nchunks; c += 8) {
-            int v[8];
+    const int64_t n = (int64_t)num_local * nch;
+    int carry = 0;
+    for (int64_t base = 0; base < n; base += 1024 * kScanPer) {
+        const int64_t i0 = base + (int64_t)tid * kScanPer;
+        int v[kScanPer];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = counts[(c + u) * num_local + e];
+        for (int q = 0; q < kScanPer / 4; ++q) {
+            int4 w = make_int4(0, 0, 0, 0);
+            if (i0 + 4 * q < n) w = *(const int4*)(counts + i0 + 4 * q);
+            v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+        }
+        int mine = 0;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) { offs[(c + u) * num_local + e] = run; run += v[u]; }
+        for (int q = 0; q < kScanPer; ++q) mine += (i0 + q < n) ? v[q] : 0;
+        int total = 0;
+        int run = carry + block_exclusive_scan(mine, scratch, &total);
+        carry += total;
+        if (i0 < n) {
+            int64_t e = i0 / nch, c = i0 - e * nch;  // (expert, chunk) of entry i0, walked along
+            int o[kScanPer];
+#pragma unroll
+            for (int q = 0; q < kScanPer; ++q) {
+                o[q] = run;
+                if (i0 + q < n) {
+                    if (c == 0) seg[e] = run;
+                    run += v[q];
+                    if (++c == nch) {
+                        c = 0;
+                        ++e;
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kScanPer / 4; ++q)
+                if (i0 + 4 * q < n) *(int4*)(offs + i0 + 4 * q) = make_int4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
         }
-        for (; c < nchunks; ++c) {
-            const int v = counts[c * num_local + e];
-            offs[c * num_local + e] = run;
-            run += v;
-        }
-        mine += run;
     }
-    int total = 0;
-    const int excl = block_exclusive_scan(mine, scratch, &total);
-    // second pass: write segment starts
-    int run = excl;
-    for (int q = 0; q < per; ++q) {
-        const int e = e0 + q;
-        if (e >= num_local) break;
-        seg[e] = run;
-        int tot_e = 0;
-        // total of expert e = offs[last] + counts[last]
-        if (nchunks > 0) tot_e = offs[(nchunks - 1) * num_local + e] + counts[(nchunks - 1) * num_local + e];
-        run += tot_e;
-    }
-    if (tid == 0) seg[num_local] = total;
+    if (tid == 0) seg[num_local] = carry;
+    if (nch == 0)
+        for (int e = tid; e < num_local; e += 1024) seg[e] = 0;
     if (per_tensor) {
         float m = 0.0f;
         for (int i = tid; i < n_part; i += 1024) m = fmaxf(m, amax_part[i]);
@@ -181,46 +192,44 @@ __global__ __launch_bounds__(1024) void pr_scan_kernel(const int32_t* __restrict
 }
 
 // ---- scatter + quantise ------------------------------------------------------------------
+__device__ __forceinline__ float amax16(const uint4& a, const uint4& b) {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[q])), fabsf(bf16_hi(w[q]))));
+    return m;
+}
+
+__device__ __forceinline__ uint4 quant16(const uint4& a, const uint4& b, float inv) {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        o[q] = quant4(bf16_lo(w[2 * q]), bf16_hi(w[2 * q]), bf16_lo(w[2 * q + 1]), bf16_hi(w[2 * q + 1]), inv);
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// One token (one wave): lanes < topk hold its pairs.
 template <int MODE>
-__global__ __launch_bounds__(256) void pr_scatter_quant_kernel(
-    const uint4* __restrict__ x, const int32_t* __restrict__ ids, int64_t T, int H, int topk,
-    int expert_start, int num_local, const int32_t* __restrict__ offs,
-    const int32_t* __restrict__ seg, int32_t* __restrict__ src2dst, int32_t* __restrict__ dst2src,
-    uint8_t* __restrict__ a_q, float* __restrict__ a_scale, const float* __restrict__ tscale,
-    int64_t m_cap) {
-    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + wid;
-
-    // rows M .. m_cap-1 of dst2src are -1 (grid-stride over the whole grid)
-    {
-        const int64_t M = seg[num_local];
-        for (int64_t r = M + (int64_t)blockIdx.x * 256 + threadIdx.x; r < m_cap;
-             r += (int64_t)gridDim.x * 256)
-            dst2src[r] = -1;
-    }
-    if (t >= T) return;
-
-    int dst = -1;
+__device__ __forceinline__ void scatter_token(
+    const uint4* __restrict__ x, const int32_t* __restrict__ ids, int64_t t, int H, int topk,
+    int expert_start, int num_local, int64_t nch, const int32_t* __restrict__ offs,
+    int32_t* __restrict__ src2dst, int32_t* __restrict__ dst2src, uint8_t* __restrict__ a_q,
+    float* __restrict__ a_scale, const float* __restrict__ tscale, int64_t m_cap, int lane) {
+    const int64_t f = t * topk + lane;
+    int e = -1;
     if (lane < topk) {
-        const int64_t f = t * topk + lane;
-        const int e = ids[f] - expert_start;
-        if (e >= 0 && e < num_local) {
-            const int64_t chunk = t / kChunkTok;
-            dst = seg[e] + offs[chunk * num_local + e] + src2dst[f];
-            // rows past m_cap exist only if a token repeats an expert; drop them
-            if (dst >= m_cap) dst = -1;
-            else dst2src[dst] = (int32_t)f;
-        }
-        src2dst[f] = dst;
+        const int ev = ids[f] - expert_start;
+        if (ev >= 0 && ev < num_local) e = ev;
     }
-    uint64_t local_mask = __ballot(dst >= 0);
-    if (local_mask == 0) return;
+    if (__ballot(e >= 0) == 0) {
+        if (lane < topk) src2dst[f] = -1;
+        return;
+    }
 
     const int G = (H + MOE_QB - 1) / MOE_QB;
     const int nit = (H + 1023) / 1024;  // iterations of 1024 columns (16 per lane)
     const uint4* xr = x + (t * H) / 8;   // 8 bf16 per uint4
-    float amax = 0.0f;
-
     auto load16 = [&](int it, uint4& a, uint4& b) {
         const int c = it * 1024 + lane * 16;
         if (c < H) {
@@ -231,22 +240,35 @@ __global__ __launch_bounds__(256) void pr_scatter_quant_kernel(
             b = a;
         }
     };
-    auto amax16 = [](const uint4& a, const uint4& b) {
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        float m = 0.0f;
+
+    // per-token mode: the whole row goes to registers now, in flight while the
+    // destination rows are looked up
+    uint4 buf[kRegIters][2];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[q])), fabsf(bf16_hi(w[q]))));
-        return m;
-    };
-    auto quant16 = [](const uint4& a, const uint4& b, float inv) {
-        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        uint32_t o[4];
+    for (int it = 0; it < kRegIters; ++it) buf[it][0] = buf[it][1] = make_uint4(0, 0, 0, 0);
+    if (MODE == MOE_ACT_PER_TOKEN) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            o[q] = quant4(bf16_lo(w[2 * q]), bf16_hi(w[2 * q]), bf16_lo(w[2 * q + 1]),
-                          bf16_hi(w[2 * q + 1]), inv);
-        return make_uint4(o[0], o[1], o[2], o[3]);
-    };
+        for (int it = 0; it < kRegIters; ++it) {
+            const int c = it * 1024 + lane * 16;
+            const int cc = c < H ? c : 0;
+            const uint4 a0 = xr[cc / 8], b0 = xr[cc / 8 + 1];
+            const bool in = c < H;
+            buf[it][0] = in ? a0 : make_uint4(0, 0, 0, 0);
+            buf[it][1] = in ? b0 : make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    int dst = -1;
+    if (e >= 0) {
+        dst = offs[(int64_t)e * nch + f / kChunkPairs] + src2dst[f];
+        // rows past m_cap exist only if a token repeats an expert; drop them
+        if (dst >= m_cap) dst = -1;
+        else dst2src[dst] = (int32_t)f;
+    }
+    if (lane < topk) src2dst[f] = dst;
+    const uint64_t local_mask = __ballot(dst >= 0);
+    if (local_mask == 0) return;
+
     auto store_rows = [&](int it, const uint4& codes) {
         const int c = it * 1024 + lane * 16;
         for (int j = 0; j < topk; ++j) {
@@ -288,17 +310,11 @@ __global__ __launch_bounds__(256) void pr_scatter_quant_kernel(
         return;
     }
 
-    // per token: pass 1 (amax), pass 2 (codes)
-    uint4 buf[kRegIters][2];
+    // per token: amax over the row, then the codes
+    float amax = 0.0f;
 #pragma unroll
-    for (int it = 0; it < kRegIters; ++it) buf[it][0] = buf[it][1] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int it = 0; it < kRegIters; ++it) {
-        if (it < nit) {
-            load16(it, buf[it][0], buf[it][1]);
-            amax = fmaxf(amax, amax16(buf[it][0], buf[it][1]));
-        }
-    }
+    for (int it = 0; it < kRegIters; ++it)
+        if (it < nit) amax = fmaxf(amax, amax16(buf[it][0], buf[it][1]));
     for (int it = kRegIters; it < nit; ++it) {
         uint4 a, b;
         load16(it, a, b);
@@ -317,9 +333,29 @@ __global__ __launch_bounds__(256) void pr_scatter_quant_kernel(
     if (lane < topk && dst >= 0) a_scale[dst] = s;
 }
 
+template <int MODE>
+__global__ __launch_bounds__(256) void pr_scatter_quant_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ ids, int64_t T, int H, int topk,
+    int expert_start, int num_local, int64_t nch, const int32_t* __restrict__ offs,
+    const int32_t* __restrict__ seg, int32_t* __restrict__ src2dst, int32_t* __restrict__ dst2src,
+    uint8_t* __restrict__ a_q, float* __restrict__ a_scale, const float* __restrict__ tscale,
+    int64_t m_cap) {
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wid;
+    const int64_t M = seg[num_local];  // needed only for the tail below
+    if (t < T)
+        scatter_token<MODE>(x, ids, t, H, topk, expert_start, num_local, nch, offs, src2dst, dst2src,
+                            a_q, a_scale, tscale, m_cap, lane);
+    // rows M .. m_cap-1 of dst2src are -1 (grid-stride over the whole grid)
+    for (int64_t r = M + (int64_t)blockIdx.x * 256 + threadIdx.x; r < m_cap; r += (int64_t)gridDim.x * 256)
+        dst2src[r] = -1;
+}
+
 }  // namespace
 
-size_t pre_reorder_ws_bytes(int64_t T, int32_t num_local) { return pre_ws_bytes(T, num_local); }
+size_t pre_reorder_ws_bytes(int64_t T, int32_t topk, int32_t num_local) {
+    return pre_ws_bytes(T, topk, num_local);
+}
 
 }  // namespace moe
 
@@ -347,17 +383,17 @@ extern "C" int moe_pre_reorder_quant(const void* x_bf16, const int32_t* topk_ids
     if (m_cap > 0 && (!a_q || !dst2src)) return MOE_ERR_NULL;
     if (want_scales > 0 && !a_scale && (m_cap > 0 || act_quant == MOE_ACT_PER_TENSOR)) return MOE_ERR_NULL;
     if ((x_bf16 && !aligned16(x_bf16)) || (a_q && !aligned16(a_q))) return MOE_ERR_INVALID_ARG;
-    const size_t need_ws = pre_ws_bytes(T, num_local);
+    const size_t need_ws = pre_ws_bytes(T, topk, num_local);
     if (!workspace || workspace_bytes < need_ws) return MOE_ERR_WORKSPACE;
 
     (void)hipGetLastError();
     hipStream_t s = (hipStream_t)stream;
-    const int64_t nch = ceil_div(T, kChunkTok);
-    PreWs ws = pre_ws_carve(workspace, T, num_local);
+    const int64_t nch = n_chunks(T, topk);
+    PreWs ws = pre_ws_carve(workspace, T, topk, num_local);
     if (nch > 0 && num_local > 0)
         hipLaunchKernelGGL(pr_count_kernel, dim3((unsigned)nch), dim3(64),
-                           sizeof(int32_t) * num_local, s, topk_ids, T, topk, expert_start,
-                           num_local, src2dst, ws.counts);
+                           sizeof(int32_t) * num_local, s, topk_ids, T * (int64_t)topk, expert_start,
+                           num_local, nch, src2dst, ws.counts);
     const int per_tensor = act_quant == MOE_ACT_PER_TENSOR;
     const int64_t n16 = T * (int64_t)H / 16;
     int n_part = 0;
@@ -373,7 +409,7 @@ extern "C" int moe_pre_reorder_quant(const void* x_bf16, const int32_t* topk_ids
     if (m_cap > 0 || T > 0) {
 #define MOE_LAUNCH_SCATTER(MODE)                                                                  \
     hipLaunchKernelGGL(pr_scatter_quant_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s,     \
-                       (const uint4*)x_bf16, topk_ids, T, H, topk, expert_start, num_local,      \
+                       (const uint4*)x_bf16, topk_ids, T, H, topk, expert_start, num_local, nch, \
                        ws.offs, seg_indptr, src2dst, dst2src, a_q, a_scale, ws.tscale, m_cap)
         if (act_quant == MOE_ACT_PER_TENSOR) MOE_LAUNCH_SCATTER(MOE_ACT_PER_TENSOR);
         else if (act_quant == MOE_ACT_PER_TOKEN) MOE_LAUNCH_SCATTER(MOE_ACT_PER_TOKEN);
