@@ -6,7 +6,8 @@
 // activation dtype and is then quantised per token, giving w2_input_scale.
 //
 // Per row and per 128-column group the whole step is one pass (h stays in
-// registers between the amax and the encode for rows up to 8192 wide). The
+// registers between the amax and the encode for rows up to 8192 wide; all of
+// a row's loads are issued before the first is used). The
 // per-tensor mode needs the maximum over all M*I values first: pass 1 writes a
 // partial maximum per block, pass 2 reduces the partials in every block and
 // recomputes h while encoding (re-reading gate/up costs the same bytes as
@@ -16,7 +17,6 @@
 namespace moe {
 namespace {
 
-constexpr int kRegIters = 8;
 constexpr int kActBlocks = 2048;  // fixed grid of the per-tensor passes (partials buffer)
 
 struct ActWs {
@@ -73,7 +73,46 @@ __device__ __forceinline__ uint4 quant16(const uint4& a, const uint4& b, float i
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-template <int MODE>  // MOE_ACT_PER_TOKEN or MOE_ACT_PER_GROUP
+// gate / up bf16 of 16 consecutive columns [c, c+16) of `row`; columns past I
+// read column 0 (a valid address) and are zeroed later by silu_mul16_from.
+struct GU16 {
+    uint4 ga, gb, ua, ub;
+};
+__device__ __forceinline__ GU16 load_gu16(const uint16_t* __restrict__ gu, int64_t row, int I, int c) {
+    const int cc = c < I ? c : 0;
+    const uint4* g4 = (const uint4*)(gu + row * 2 * (int64_t)I + cc);
+    const uint4* u4 = (const uint4*)(gu + row * 2 * (int64_t)I + I + cc);
+    GU16 v;
+    v.ga = g4[0];
+    v.gb = g4[1];
+    v.ua = u4[0];
+    v.ub = u4[1];
+    return v;
+}
+__device__ __forceinline__ void silu_mul16_from(const GU16& v, int I, int c, uint4& h0, uint4& h1) {
+    if (c >= I) {
+        h0 = make_uint4(0, 0, 0, 0);
+        h1 = h0;
+        return;
+    }
+    const uint32_t g[8] = {v.ga.x, v.ga.y, v.ga.z, v.ga.w, v.gb.x, v.gb.y, v.gb.z, v.gb.w};
+    const uint32_t u[8] = {v.ua.x, v.ua.y, v.ua.z, v.ua.w, v.ub.x, v.ub.y, v.ub.z, v.ub.w};
+    uint32_t h[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float g0 = bf16_lo(g[q]), g1 = bf16_hi(g[q]);
+        const float u0 = bf16_lo(u[q]), u1 = bf16_hi(u[q]);
+        const float s0 = g0 / (1.0f + exp_fixed(-g0));
+        const float s1 = g1 / (1.0f + exp_fixed(-g1));
+        h[q] = f32_to_bf16_bits(s0 * u0) | (f32_to_bf16_bits(s1 * u1) << 16);
+    }
+    h0 = make_uint4(h[0], h[1], h[2], h[3]);
+    h1 = make_uint4(h[4], h[5], h[6], h[7]);
+}
+
+// One wave per row, rows up to NIT * 1024 columns: all of a row's gate / up
+// loads are issued before any of them is used.
+template <int MODE, int NIT>  // MODE: MOE_ACT_PER_TOKEN or MOE_ACT_PER_GROUP
 __global__ __launch_bounds__(256) void act_requant_kernel(const uint16_t* __restrict__ gu,
                                                           const int32_t* __restrict__ seg,
                                                           int num_local, int64_t m_cap, int I,
@@ -81,50 +120,77 @@ __global__ __launch_bounds__(256) void act_requant_kernel(const uint16_t* __rest
                                                           float* __restrict__ a_scale) {
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t M = rows_present(seg, num_local, m_cap);
-    const int nit = (I + 1023) / 1024;
     const int G = (I + MOE_QB - 1) / MOE_QB;
     for (int64_t row = (int64_t)blockIdx.x * 4 + wid; row < M; row += (int64_t)gridDim.x * 4) {
         uint8_t* out = a_q + row * I;
+        GU16 v[NIT];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) v[it] = load_gu16(gu, row, I, it * 1024 + lane * 16);
+        uint4 hb[NIT][2];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) silu_mul16_from(v[it], I, it * 1024 + lane * 16, hb[it][0], hb[it][1]);
         if (MODE == MOE_ACT_PER_GROUP) {
-            for (int it = 0; it < nit; ++it) {
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
                 const int c = it * 1024 + lane * 16;
-                uint4 h0, h1;
-                silu_mul16(gu, row, I, c, h0, h1);
                 float s, inv;
-                dyn_scale(group8_max(amax16(h0, h1)), s, inv);
-                if (c < I) *(uint4*)(out + c) = quant16(h0, h1, inv);
+                dyn_scale(group8_max(amax16(hb[it][0], hb[it][1])), s, inv);
+                if (c < I) *(uint4*)(out + c) = quant16(hb[it][0], hb[it][1], inv);
                 const int g = it * 8 + (lane >> 3);
                 if ((lane & 7) == 0 && g < G) a_scale[row * G + g] = s;
             }
             continue;
         }
-        uint4 hb[kRegIters][2];
         float amax = 0.0f;
 #pragma unroll
-        for (int it = 0; it < kRegIters; ++it)
-            if (it < nit) {
-                silu_mul16(gu, row, I, it * 1024 + lane * 16, hb[it][0], hb[it][1]);
-                amax = fmaxf(amax, amax16(hb[it][0], hb[it][1]));
-            }
-        for (int it = kRegIters; it < nit; ++it) {
-            uint4 h0, h1;
-            silu_mul16(gu, row, I, it * 1024 + lane * 16, h0, h1);
-            amax = fmaxf(amax, amax16(h0, h1));
-        }
+        for (int it = 0; it < NIT; ++it) amax = fmaxf(amax, amax16(hb[it][0], hb[it][1]));
         float s, inv;
         dyn_scale(wave_max(amax), s, inv);
 #pragma unroll
-        for (int it = 0; it < kRegIters; ++it) {
+        for (int it = 0; it < NIT; ++it) {
             const int c = it * 1024 + lane * 16;
-            if (it < nit && c < I) *(uint4*)(out + c) = quant16(hb[it][0], hb[it][1], inv);
+            if (c < I) *(uint4*)(out + c) = quant16(hb[it][0], hb[it][1], inv);
         }
-        for (int it = kRegIters; it < nit; ++it) {
+        if (lane == 0) a_scale[row] = s;
+    }
+}
+
+// Rows wider than 8192 columns (per token / per group): streamed, two passes
+// over the row for the per-token maximum.
+template <int MODE>
+__global__ __launch_bounds__(256) void act_requant_wide_kernel(const uint16_t* __restrict__ gu,
+                                                               const int32_t* __restrict__ seg,
+                                                               int num_local, int64_t m_cap, int I,
+                                                               uint8_t* __restrict__ a_q,
+                                                               float* __restrict__ a_scale) {
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t M = rows_present(seg, num_local, m_cap);
+    const int nit = (I + 1023) / 1024;
+    const int G = (I + MOE_QB - 1) / MOE_QB;
+    for (int64_t row = (int64_t)blockIdx.x * 4 + wid; row < M; row += (int64_t)gridDim.x * 4) {
+        uint8_t* out = a_q + row * I;
+        float s = 0.0f, inv = 0.0f;
+        if (MODE == MOE_ACT_PER_TOKEN) {
+            float amax = 0.0f;
+            for (int it = 0; it < nit; ++it) {
+                uint4 h0, h1;
+                silu_mul16(gu, row, I, it * 1024 + lane * 16, h0, h1);
+                amax = fmaxf(amax, amax16(h0, h1));
+            }
+            dyn_scale(wave_max(amax), s, inv);
+        }
+        for (int it = 0; it < nit; ++it) {
             const int c = it * 1024 + lane * 16;
             uint4 h0, h1;
             silu_mul16(gu, row, I, c, h0, h1);
+            if (MODE == MOE_ACT_PER_GROUP) {
+                dyn_scale(group8_max(amax16(h0, h1)), s, inv);
+                const int g = it * 8 + (lane >> 3);
+                if ((lane & 7) == 0 && g < G) a_scale[row * G + g] = s;
+            }
             if (c < I) *(uint4*)(out + c) = quant16(h0, h1, inv);
         }
-        if (lane == 0) a_scale[row] = s;
+        if (MODE == MOE_ACT_PER_TOKEN && lane == 0) a_scale[row] = s;
     }
 }
 
@@ -218,11 +284,27 @@ extern "C" int moe_act_requant(const void* gateup_bf16, const int32_t* seg_indpt
     const int64_t cap = (int64_t)device_cu_count() * 16;
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
-    if (act_quant == MOE_ACT_PER_TOKEN)
-        hipLaunchKernelGGL(act_requant_kernel<MOE_ACT_PER_TOKEN>, dim3((unsigned)grid), dim3(256), 0,
-                           s, gu, seg_indptr, num_local, m_cap, I, a_q, a_scale);
-    else
-        hipLaunchKernelGGL(act_requant_kernel<MOE_ACT_PER_GROUP>, dim3((unsigned)grid), dim3(256), 0,
-                           s, gu, seg_indptr, num_local, m_cap, I, a_q, a_scale);
+    const int nit = (int)ceil_div(I, 1024);
+#define MOE_LAUNCH_ACT(MODE)                                                                        \
+    do {                                                                                            \
+        if (nit <= 1)                                                                               \
+            hipLaunchKernelGGL((act_requant_kernel<MODE, 1>), dim3((unsigned)grid), dim3(256), 0, s, gu, \
+                               seg_indptr, num_local, m_cap, I, a_q, a_scale);                     \
+        else if (nit <= 2)                                                                          \
+            hipLaunchKernelGGL((act_requant_kernel<MODE, 2>), dim3((unsigned)grid), dim3(256), 0, s, gu, \
+                               seg_indptr, num_local, m_cap, I, a_q, a_scale);                     \
+        else if (nit <= 4)                                                                          \
+            hipLaunchKernelGGL((act_requant_kernel<MODE, 4>), dim3((unsigned)grid), dim3(256), 0, s, gu, \
+                               seg_indptr, num_local, m_cap, I, a_q, a_scale);                     \
+        else if (nit <= 8)                                                                          \
+            hipLaunchKernelGGL((act_requant_kernel<MODE, 8>), dim3((unsigned)grid), dim3(256), 0, s, gu, \
+                               seg_indptr, num_local, m_cap, I, a_q, a_scale);                     \
+        else                                                                                        \
+            hipLaunchKernelGGL((act_requant_wide_kernel<MODE>), dim3((unsigned)grid), dim3(256), 0, s, gu, \
+                               seg_indptr, num_local, m_cap, I, a_q, a_scale);                     \
+    } while (0)
+    if (act_quant == MOE_ACT_PER_TOKEN) MOE_LAUNCH_ACT(MOE_ACT_PER_TOKEN);
+    else MOE_LAUNCH_ACT(MOE_ACT_PER_GROUP);
+#undef MOE_LAUNCH_ACT
     return launch_status();
 }

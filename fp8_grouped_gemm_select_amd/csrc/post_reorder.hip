@@ -11,6 +11,70 @@
 namespace moe {
 namespace {
 
+// topk <= 8: each lane covers 16 columns (32 bytes) per iteration; the loads of
+// every local slot of an iteration are issued together, then accumulated in
+// slot order (the same fp32 order as the general kernel below).
+__global__ __launch_bounds__(256) void post_reorder8_kernel(const uint16_t* __restrict__ down,
+                                                            const int32_t* __restrict__ src2dst,
+                                                            const float* __restrict__ w, int64_t T,
+                                                            int H, int topk, int64_t m_cap,
+                                                            uint16_t* __restrict__ out) {
+    constexpr int K8 = 8;
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wid;
+    if (t >= T) return;
+    int r = -1;
+    float wt = 0.0f;
+    if (lane < topk) {
+        const int32_t v = src2dst[t * topk + lane];
+        if (v >= 0 && v < m_cap) {
+            r = v;
+            wt = w[t * topk + lane];
+        }
+    }
+    const uint64_t mask = __ballot(r >= 0);
+    int rows[K8];
+    float wj[K8];
+#pragma unroll
+    for (int j = 0; j < K8; ++j) {
+        rows[j] = __builtin_amdgcn_readlane(r, j);
+        wj[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), j));
+    }
+    for (int c = lane * 16; c < H; c += 1024) {
+        uint4 v[K8][2];
+#pragma unroll
+        for (int j = 0; j < K8; ++j) {
+            if ((mask >> j) & 1ull) {
+                const uint4* p = (const uint4*)(down + (int64_t)rows[j] * H + c);
+                v[j][0] = p[0];
+                v[j][1] = p[1];
+            }
+        }
+        float acc[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < K8; ++j) {
+            if ((mask >> j) & 1ull) {
+                const uint32_t d[8] = {v[j][0].x, v[j][0].y, v[j][0].z, v[j][0].w,
+                                       v[j][1].x, v[j][1].y, v[j][1].z, v[j][1].w};
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    acc[2 * q] = acc[2 * q] + wj[j] * bf16_lo(d[q]);
+                    acc[2 * q + 1] = acc[2 * q + 1] + wj[j] * bf16_hi(d[q]);
+                }
+            }
+        }
+        uint32_t o[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = f32_to_bf16_bits(acc[2 * q]) | (f32_to_bf16_bits(acc[2 * q + 1]) << 16);
+        uint4* po = (uint4*)(out + t * H + c);
+        po[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        po[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+// any topk: one 16-byte column group per lane per iteration, slots one by one
 __global__ __launch_bounds__(256) void post_reorder_kernel(const uint16_t* __restrict__ down,
                                                            const int32_t* __restrict__ src2dst,
                                                            const float* __restrict__ w, int64_t T,
@@ -67,8 +131,13 @@ extern "C" int moe_post_reorder(const void* down_bf16, const int32_t* src2dst,
     if (!src2dst || !topk_weights || !out_bf16 || (m_cap > 0 && !down_bf16)) return MOE_ERR_NULL;
     if ((down_bf16 && !aligned16(down_bf16)) || !aligned16(out_bf16)) return MOE_ERR_INVALID_ARG;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(post_reorder_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
-                       (hipStream_t)stream, (const uint16_t*)down_bf16, src2dst, topk_weights, T,
-                       H, topk, m_cap, (uint16_t*)out_bf16);
+    if (topk <= 8)
+        hipLaunchKernelGGL(post_reorder8_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
+                           (hipStream_t)stream, (const uint16_t*)down_bf16, src2dst, topk_weights, T,
+                           H, topk, m_cap, (uint16_t*)out_bf16);
+    else
+        hipLaunchKernelGGL(post_reorder_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
+                           (hipStream_t)stream, (const uint16_t*)down_bf16, src2dst, topk_weights, T,
+                           H, topk, m_cap, (uint16_t*)out_bf16);
     return launch_status();
 }

@@ -17,6 +17,41 @@ __device__ __forceinline__ bool ranks_before(float ka, int ia, float kb, int ib)
     return ka > kb || (ka == kb && ia < ib);
 }
 
+// Cross-lane moves without LDS: DPP within rows of 16 lanes, and the gfx950
+// permlane swaps across rows and halves of the wave.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16
+
+// wave-wide maximum, in every lane
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppMirror>(v));
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+// merge two descending pairs (a1 >= a2, b1 >= b2) into the top two of the four
+__device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float b2) {
+    const float n1 = fmaxf(a1, b1);
+    const float n2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
+    a1 = n1;
+    a2 = n2;
+}
+template <int CTRL>
+__device__ __forceinline__ void top2_step(float& a1, float& a2) {
+    top2_merge(a1, a2, dpp<CTRL>(a1), dpp<CTRL>(a2));
+}
+
 // Each lane owns EPL consecutive experts: e = lane*EPL + i.
 template <int EPL>
 __global__ __launch_bounds__(256) void select_experts_kernel(
@@ -48,7 +83,30 @@ __global__ __launch_bounds__(256) void select_experts_kernel(
     }
 
     // ---- group-limited selection ----
-    if (n_group > 1) {
+    // Fast path: a group spans LPG = (E / n_group) / EPL lanes, LPG in {1, 2, 4, 8}:
+    // the top two biased keys of the group come from a DPP merge over its lanes,
+    // and each lane ranks its group against all group scores (readlane).
+    const int gsz = n_group > 1 ? E / n_group : E;
+    const int lpg = gsz % EPL == 0 ? gsz / EPL : 0;
+    if (n_group > 1 && (lpg == 1 || lpg == 2 || lpg == 4 || lpg == 8)) {
+        float t1 = -INFINITY, t2 = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (lane * EPL + i < E) top2_merge(t1, t2, key[i], -INFINITY);
+        if (lpg >= 2) top2_step<kDppXor1>(t1, t2);
+        if (lpg >= 4) top2_step<kDppXor2>(t1, t2);
+        if (lpg >= 8) top2_step<kDppHalfMirror>(t1, t2);
+        const float gscore = gsz >= 2 ? t1 + t2 : t1;
+        const int g = lane / lpg;
+        int rank = 0;
+        for (int g2 = 0; g2 < n_group; ++g2) {
+            const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gscore), g2 * lpg));
+            rank += (o > gscore || (o == gscore && g2 < g)) ? 1 : 0;
+        }
+        const bool keep = rank < topk_group;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) ok[i] = ok[i] && keep;
+    } else if (n_group > 1) {
 #pragma unroll
         for (int i = 0; i < EPL; ++i) s_key[wid][lane * EPL + i] = key[i];
         __syncthreads();
@@ -86,28 +144,28 @@ __global__ __launch_bounds__(256) void select_experts_kernel(
     }
 
     // ---- top-k over the allowed experts ----
+    // Round j: each lane's best allowed key (lowest index among equals), the
+    // wave maximum by DPP, and the lowest lane holding it (ballot) owns the
+    // winner: larger key first, equal keys by lower expert id.
     int my_id = 0;
     float my_sc = 0.0f;
     for (int j = 0; j < topk; ++j) {
-        float bk = -INFINITY, bs = 0.0f;
-        int bi = 0x7fffffff;
+        float lb = -INFINITY, lsc = 0.0f;
+        int li = -1;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int e = lane * EPL + i;
-            if (ok[i] && ranks_before(key[i], e, bk, bi)) { bk = key[i]; bi = e; bs = sc[i]; }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ok2 = __shfl_xor(bk, o, MOE_WAVE);
-            const int oi = __shfl_xor(bi, o, MOE_WAVE);
-            const float os = __shfl_xor(bs, o, MOE_WAVE);
-            if (ranks_before(ok2, oi, bk, bi)) { bk = ok2; bi = oi; bs = os; }
-        }
-        if (lane == j) { my_id = bi; my_sc = bs; }
-        if (bi / EPL == lane) {
+        for (int i = 0; i < EPL; ++i)
+            if (ok[i] && (li < 0 || key[i] > lb)) { lb = key[i]; li = i; lsc = sc[i]; }
+        const float m = wave_max_dpp(li >= 0 ? lb : -INFINITY);
+        const uint64_t owners = __ballot(li >= 0 && lb == m);
+        if (owners == 0) break;
+        const int owner = __ffsll((unsigned long long)owners) - 1;
+        const int wi = __builtin_amdgcn_readlane(li, owner);
+        const float wsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsc), owner));
+        if (lane == j) { my_id = owner * EPL + wi; my_sc = wsc; }
+        if (lane == owner) {
 #pragma unroll
             for (int i = 0; i < EPL; ++i)
-                if (lane * EPL + i == bi) ok[i] = false;
+                if (i == wi) ok[i] = false;
         }
     }
 

@@ -299,7 +299,8 @@ def test_grouped_gemm_full_size_sampled_rows(name, which):
 # ---- stage 4 ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("act_quant", [W.ACT_PER_TENSOR, W.ACT_PER_TOKEN, W.ACT_PER_GROUP])
-@pytest.mark.parametrize("dims", [((20, 0, 31), 64), ((300, 17), 2048), ((5,), 9216), ((64, 64), 768)])
+@pytest.mark.parametrize("dims", [((20, 0, 31), 64), ((300, 17), 2048), ((5,), 9216), ((64, 64), 768),
+                                  ((7, 3), 3072), ((9,), 5120)])
 def test_act_requant_ragged(act_quant, dims):
     counts, I = dims
     g = np.random.default_rng(len(counts) * 100 + I)
@@ -352,3 +353,25 @@ def test_post_reorder(name):
     G.assert_sum_close(out, ref, abs_terms, cfg.topk, what="combine", mfma=False)
     none = np.all(s2d.reshape(cfg.T, cfg.topk) < 0, axis=1)
     assert np.all(out[none] == 0)
+
+
+def test_post_reorder_many_slots():
+    """topk above 8 takes the general combine kernel: random local slots, some
+    slots non-local (-1), H not a multiple of the 1024-column step."""
+    g = np.random.default_rng(6)
+    T, topk, H, m_cap = 37, 12, 144, 37 * 12
+    perm = g.permutation(m_cap).astype(np.int32)
+    s2d = np.where(g.random(T * topk) < 0.3, -1, perm).astype(np.int32)
+    w = g.uniform(0.0, 1.0, (T, topk)).astype(np.float32)
+    down = W.to_bf16_bits(g.standard_normal((m_cap, H), dtype=np.float32))
+    print(f"post_reorder general kernel T={T} topk={topk} H={H}", flush=True)
+    ref = oracle.post_reorder(down, s2d, w, T, topk)
+    out = G.run_post(down, s2d, w, T, topk)
+    d = np.abs(G.bf16_to_f64(down))
+    sd = s2d.reshape(T, topk)
+    abs_terms = np.zeros((T, H))
+    for j in range(topk):
+        ok = sd[:, j] >= 0
+        abs_terms[ok] += np.abs(w[ok, j].astype(np.float64))[:, None] * d[sd[ok, j]]
+    G.assert_sum_close(out, ref, abs_terms, topk, what="combine", mfma=False)
+    assert np.all(out[np.all(sd < 0, axis=1)] == 0)
