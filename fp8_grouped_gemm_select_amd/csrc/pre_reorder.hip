@@ -150,26 +150,18 @@ __global__ __launch_bounds__(1024) void pr_scan_kernel(const int32_t* __restrict
         int total = 0;
         int run = carry + block_exclusive_scan(mine, scratch, &total);
         carry += total;
-        if (i0 < n) {
-            int64_t e = i0 / nch, c = i0 - e * nch;  // (expert, chunk) of entry i0, walked along
-            int o[kScanPer];
+        int o[kScanPer];
 #pragma unroll
-            for (int q = 0; q < kScanPer; ++q) {
-                o[q] = run;
-                if (i0 + q < n) {
-                    if (c == 0) seg[e] = run;
-                    run += v[q];
-                    if (++c == nch) {
-                        c = 0;
-                        ++e;
-                    }
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < kScanPer / 4; ++q)
-                if (i0 + 4 * q < n) *(int4*)(offs + i0 + 4 * q) = make_int4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        for (int q = 0; q < kScanPer; ++q) {
+            o[q] = run;
+            run += (i0 + q < n) ? v[q] : 0;
         }
+#pragma unroll
+        for (int q = 0; q < kScanPer / 4; ++q)
+            if (i0 + 4 * q < n) *(int4*)(offs + i0 + 4 * q) = make_int4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
     }
+    __syncthreads();  // offs written by the block is visible to all of it
+    for (int e = tid; e < num_local && nch > 0; e += 1024) seg[e] = offs[(int64_t)e * nch];
     if (tid == 0) seg[num_local] = carry;
     if (nch == 0)
         for (int e = tid; e < num_local; e += 1024) seg[e] = 0;
