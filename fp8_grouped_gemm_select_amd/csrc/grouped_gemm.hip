@@ -327,6 +327,14 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
 }
 
+// Per-tile state of the large-tile kernel: coordinates and per-lane DMA offsets.
+struct DTile {
+    int e, row0, row_end, n0, a_rows, b_rows, sa_row, nb_w;
+    const uint8_t* a_g;
+    const uint8_t* b_g;
+    uint32_t a_off[kDmaA], b_off[kDmaB];
+};
+
 template <bool KDEP>
 __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, int act_quant,
@@ -346,6 +354,8 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
     const int NB = (N + MOE_QB - 1) / MOE_QB;
     const int nk = K / DBK;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const void*)lds;
+    const bool group_act = KDEP && act_quant == MOE_ACT_PER_GROUP;
+    const bool block_w = KDEP && w_quant == MOE_W_BLOCK;
 
     const int total = build_tile_table<DBM, DBN>(seg_in, num_local, m_cap, N, s_seg, s_tstart, scan_scratch);
 
@@ -354,47 +364,81 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
     const int lt_begin = xcd * per_xcd;
     const int lt_end = lt_begin + per_xcd < total ? lt_begin + per_xcd : total;
 
-    for (int lt = lt_begin + slot; lt < lt_end; lt += per_xcd_blocks) {
+    auto setup = [&](int lt) {
         const TileCoord tc = tile_coord<DBM, DBN>(lt, s_seg, s_tstart, num_local);
-        const int e = tc.e, row0 = tc.row0, row_end = tc.row_end, n0 = tc.n0;
-        const int a_rows = row_end - row0, b_rows = N - n0 < DBN ? N - n0 : DBN;
-        const bool group_act = KDEP && act_quant == MOE_ACT_PER_GROUP;
-        const bool block_w = KDEP && w_quant == MOE_W_BLOCK;
+        DTile t;
+        t.e = tc.e;
+        t.row0 = tc.row0;
+        t.row_end = tc.row_end;
+        t.n0 = tc.n0;
+        t.a_rows = tc.row_end - tc.row0;
+        t.b_rows = N - tc.n0 < DBN ? N - tc.n0 : DBN;
         // the weight-scale block of this wave's 64 columns (clamped: in a partial
         // tile a wave's columns can start past N; its outputs are not stored)
-        const int nb_w = (n0 + wn * 64) / MOE_QB < NB ? (n0 + wn * 64) / MOE_QB : NB - 1;
-
+        t.nb_w = (t.n0 + wn * 64) / MOE_QB < NB ? (t.n0 + wn * 64) / MOE_QB : NB - 1;
         // per-lane DMA offsets: instruction i of this wave fills LDS rows
         // 8 * (wave's first block + i) + lane / 8, chunk position lane % 8, which
         // holds global chunk (lane % 8) ^ perm8(row)
-        uint32_t a_off[kDmaA], b_off[kDmaB];
 #pragma unroll
         for (int i = 0; i < kDmaA; ++i) {
             const int r = (wid * kDmaA + i) * 8 + (lane >> 3);
-            const int g = r < a_rows ? r : a_rows - 1;
-            a_off[i] = (uint32_t)g * (uint32_t)K + (uint32_t)((((lane & 7) ^ perm8(r)) << 4));
+            const int g = r < t.a_rows ? r : t.a_rows - 1;
+            t.a_off[i] = (uint32_t)g * (uint32_t)K + (uint32_t)((((lane & 7) ^ perm8(r)) << 4));
         }
 #pragma unroll
         for (int i = 0; i < kDmaB; ++i) {
             const int r = (wid * kDmaB + i) * 8 + (lane >> 3);
-            const int g = r < b_rows ? r : b_rows - 1;
-            b_off[i] = (uint32_t)g * (uint32_t)K + (uint32_t)((((lane & 7) ^ perm8(r)) << 4));
+            const int g = r < t.b_rows ? r : t.b_rows - 1;
+            t.b_off[i] = (uint32_t)g * (uint32_t)K + (uint32_t)((((lane & 7) ^ perm8(r)) << 4));
         }
-        const uint8_t* a_g = A + (int64_t)row0 * K;
-        const uint8_t* b_g = B + ((int64_t)e * N + n0) * K;
-        const int sa_row = row0 + ((tid & (DBM - 1)) < a_rows ? (tid & (DBM - 1)) : a_rows - 1);
+        t.a_g = A + (int64_t)t.row0 * K;
+        t.b_g = B + ((int64_t)t.e * N + t.n0) * K;
+        t.sa_row = t.row0 + ((tid & (DBM - 1)) < t.a_rows ? (tid & (DBM - 1)) : t.a_rows - 1);
+        return t;
+    };
+    auto issue = [&](const DTile& t, int k) {  // DMA of K step k into stage k % 3
+        const uint32_t st = lds0 + (uint32_t)((k % kDStages) * kDStage);
+        const uint8_t* ab = uniform_ptr(t.a_g + k * DBK);
+        const uint8_t* bb = uniform_ptr(t.b_g + k * DBK);
+        const uint32_t la = __builtin_amdgcn_readfirstlane(st + wid * kDmaA * 1024);
+        const uint32_t lb = __builtin_amdgcn_readfirstlane(st + kDStageA + wid * kDmaB * 1024);
+#pragma unroll
+        for (int i = 0; i < kDmaA; ++i) dma16(ab, t.a_off[i], la + i * 1024);
+#pragma unroll
+        for (int i = 0; i < kDmaB; ++i) dma16(bb, t.b_off[i], lb + i * 1024);
+    };
 
-        auto issue = [&](int k) {  // DMA of K step k into stage k % 3
-            const uint32_t st = lds0 + (uint32_t)((k % kDStages) * kDStage);
-            const uint8_t* ab = uniform_ptr(a_g + k * DBK);
-            const uint8_t* bb = uniform_ptr(b_g + k * DBK);
-            const uint32_t la = __builtin_amdgcn_readfirstlane(st + wid * kDmaA * 1024);
-            const uint32_t lb = __builtin_amdgcn_readfirstlane(st + kDStageA + wid * kDmaB * 1024);
+    int lt = lt_begin + slot;
+    if (lt >= lt_end) return;  // the whole block has no tile
+
+    // Issue order: [activation group scales of step j+1] [DMA of step j+2] per
+    // step j, after the first tile's [scales 0] [DMA 0] [DMA 1]; a following
+    // tile's [scales 0] [DMA 0] [DMA 1] go out before the previous tile's
+    // epilogue (whose stores come after them). At step k the wave needs DMA(k)
+    // and the scales of step k; at most DMA(k+1) and epilogue stores were
+    // issued after them, so vmcnt(kDma) suffices while k + 1 < nk (it may also
+    // wait for some of those stores, never for less than it needs).
+    DTile cur = setup(lt);
+    float q = 0.f;
+    if (group_act) q = sa[(int64_t)cur.sa_row * KB];
+    issue(cur, 0);
+    if (nk > 1) issue(cur, 1);
+
+    while (true) {
+        // epilogue scales of this tile, in flight during the K loop
+        float srow[4], scol[4][4];
 #pragma unroll
-            for (int i = 0; i < kDmaA; ++i) dma16(ab, a_off[i], la + i * 1024);
+        for (int i = 0; i < 4; ++i) {
+            const int r = cur.row0 + wm * 64 + i * 16 + (lane & 15);
+            srow[i] = group_act ? 1.0f : (act_quant == MOE_ACT_PER_TENSOR ? sa[0] : sa[r < cur.row_end ? r : cur.row0]);
+        }
 #pragma unroll
-            for (int i = 0; i < kDmaB; ++i) dma16(bb, b_off[i], lb + i * 1024);
-        };
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int n = cur.n0 + wn * 64 + j * 16 + (lane >> 4) * 4 + v;
+                scol[j][v] = block_w ? 1.0f : (w_quant == MOE_W_PER_EXPERT ? sb[cur.e] : sb[(int64_t)cur.e * N + (n < N ? n : N - 1)]);
+            }
 
         v4f acc[4][4];
 #pragma unroll
@@ -402,21 +446,13 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        // Issue order per step j: [activation group scales of step j+1] [DMA of
-        // step j+2]. At step k the wave needs DMA(k) (issued at step k-2) and
-        // the scales of step k (issued at step k-1); only DMA(k+1) was issued
-        // after them, so vmcnt(kDma) suffices while k + 1 < nk.
-        float q = 0.f;
-        if (group_act) q = sa[(int64_t)sa_row * KB];
-        issue(0);
-        if (nk > 1) issue(1);
         for (int k = 0; k < nk; ++k) {
             if (k + 1 < nk) wait_vmcnt<kDma>();
             else wait_vmcnt<0>();
             if (group_act && tid < DBM) s_sa[k % kDStages][tid] = q;
             __syncthreads();  // stage k complete; every wave is done with stage k-1
-            if (group_act && k + 1 < nk) q = sa[(int64_t)sa_row * KB + k + 1];
-            if (k + 2 < nk) issue(k + 2);
+            if (group_act && k + 1 < nk) q = sa[(int64_t)cur.sa_row * KB + k + 1];
+            if (k + 2 < nk) issue(cur, k + 2);
 
             const uint8_t* la = lds + (k % kDStages) * kDStage;
             const uint8_t* lb = la + kDStageA;
@@ -434,7 +470,7 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             bfr[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
             } else {
-                const float sbv = block_w ? sb[((int64_t)e * NB + nb_w) * KB + k] : 1.0f;
+                const float sbv = block_w ? sb[((int64_t)cur.e * NB + cur.nb_w) * KB + k] : 1.0f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float f = (group_act ? s_sa[k % kDStages][wm * 64 + i * 16 + (lane & 15)] : 1.0f) * sbv;
@@ -450,40 +486,50 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
         }
         __syncthreads();  // every wave is done with the operand stages
 
-        // ---- epilogue: remaining scales, bf16 into LDS, 16-byte row stores ----
-        uint8_t* ep = lds + wid * (64 * 128);
+        // next tile: its first two stages (slots 0 and 1) load during this epilogue
+        const int lt_next = lt + per_xcd_blocks;
+        const bool has_next = lt_next < lt_end;
+        DTile nxt;
+        if (has_next) {
+            nxt = setup(lt_next);
+            if (group_act) q = sa[(int64_t)nxt.sa_row * KB];
+            issue(nxt, 0);
+            if (nk > 1) issue(nxt, 1);
+        }
+
+        // ---- epilogue: scales, bf16 into LDS slot 2, 16-byte row stores, in two
+        // halves of 32 rows per wave (4 KB per wave) ----
+        uint8_t* ep = lds + 2 * kDStage + wid * (32 * 128);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rl = i * 16 + (lane & 15);
-            const int r = row0 + wm * 64 + rl;
-            float srow = 1.0f;
-            if (!group_act) srow = act_quant == MOE_ACT_PER_TENSOR ? sa[0] : sa[r < row_end ? r : row0];
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int cl = j * 16 + (lane >> 4) * 4;
-                uint32_t h[4];
+            for (int ii = 0; ii < 2; ++ii) {
+                const int i = 2 * h + ii;
+                const int rl = ii * 16 + (lane & 15);  // row within the half
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    float scol = 1.0f;
-                    if (!block_w) {
-                        const int n = n0 + wn * 64 + cl + v;
-                        scol = w_quant == MOE_W_PER_EXPERT ? sb[e] : sb[(int64_t)e * N + (n < N ? n : N - 1)];
-                    }
-                    h[v] = f32_to_bf16_bits(acc[i][j][v] * (srow * scol));
+                for (int j = 0; j < 4; ++j) {
+                    const int cl = j * 16 + (lane >> 4) * 4;
+                    uint32_t hb[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) hb[v] = f32_to_bf16_bits(acc[i][j][v] * (srow[i] * scol[j][v]));
+                    *(uint2*)(ep + ep_off(rl, cl >> 3) + (cl & 7) * 2) =
+                        make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
                 }
-                *(uint2*)(ep + ep_off(rl, cl >> 3) + (cl & 7) * 2) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             }
-        }
-        __syncthreads();  // the staged blocks are complete (lanes read other lanes' values)
+            __syncthreads();  // the staged half is complete (lanes read other lanes' values)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int rl = t * 8 + (lane >> 3), qc = lane & 7;
-            const int r = row0 + wm * 64 + rl;
-            const int n = n0 + wn * 64 + qc * 8;
-            const uint4 v = *(const uint4*)(ep + ep_off(rl, qc));
-            if (r < row_end && n < N) *(uint4*)(C + (int64_t)r * N + n) = v;
+            for (int t = 0; t < 4; ++t) {
+                const int rl = t * 8 + (lane >> 3), qc = lane & 7;
+                const int r = cur.row0 + wm * 64 + h * 32 + rl;
+                const int n = cur.n0 + wn * 64 + qc * 8;
+                const uint4 v = *(const uint4*)(ep + ep_off(rl, qc));
+                if (r < cur.row_end && n < N) *(uint4*)(C + (int64_t)r * N + n) = v;
+            }
+            __syncthreads();  // the half has been read back before the slot is reused
         }
-        __syncthreads();  // the LDS is free for the next tile's stages
+        if (!has_next) break;
+        cur = nxt;
+        lt = lt_next;
     }
 }
 
