@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "EP-MoE layer tokens/s at 1 GPU; grouped FP8 GEMM TFLOP/s as % of MFMA peak"
 
 
@@ -37,6 +38,8 @@ def parse():
     p.add_argument("--config", default="dsv3_prefill_ep")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-next-rows", action="store_true",
+                   help="skip the separately timed extension rows (router projection)")
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
                    help="tokens in the oracle's timed sample (0: per-workload default)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -200,6 +203,9 @@ def main():
         "roofline": roof, "gemm": gemm, "stages": stage_stats,
     }
 
+    if not args.no_next_rows:
+        result["next_rows"] = {"router_select": time_router_select(cfg, inp, args, moe, W, torch, dev)}
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -213,6 +219,39 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)
+
+
+def time_router_select(cfg, inp, args, moe, W, torch, dev):
+    """The router projection + stage 1 from the hidden states (an extension row,
+    not part of the five-stage step): its own timed loop on the same stream."""
+    wg = torch.from_numpy(W.gen_router_bf16(cfg, args.seed).view(np.int16)).to(dev).view(torch.bfloat16)
+    x = torch.from_numpy(inp.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    bias = torch.from_numpy(inp.bias).to(dev) if inp.bias is not None else None
+    logits = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=dev)
+    ids = torch.empty(cfg.T, cfg.topk, dtype=torch.int32, device=dev)
+    w = torch.empty(cfg.T, cfg.topk, dtype=torch.float32, device=dev)
+
+    def run():
+        moe.moe_router_select(x, wg, bias, logits, ids, w, topk=cfg.topk, n_group=cfg.n_group,
+                              topk_group=cfg.topk_group, score_fn=cfg.score_fn,
+                              renormalize=cfg.renormalize, routed_scaling_factor=cfg.rsf,
+                              apply_rsf=cfg.apply_rsf)
+    for _ in range(3):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / args.steps
+    byts = cfg.T * cfg.H * 2 + cfg.E * cfg.H * 2 + 2 * cfg.T * cfg.E * 4 + cfg.T * cfg.topk * 8
+    flops = 2 * cfg.T * cfg.H * cfg.E
+    return dict(us=round(t * 1e6, 2), GBps=round(byts / t / 1e9, 1), hbm_frac=round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
+                TFLOPs=round(flops / t / 1e12, 1), bf16_mfma_frac=round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+                algorithmic_bytes=int(byts), flops=int(flops),
+                note="bf16 router projection x @ wg^T + stage 1, timed on its own, not in value")
 
 
 def measured_traffic(workload, stage):

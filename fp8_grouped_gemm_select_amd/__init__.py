@@ -30,7 +30,8 @@ ACT_PER_TENSOR, ACT_PER_TOKEN, ACT_PER_GROUP = 0, 1, 2
 W_PER_EXPERT, W_PER_CHANNEL, W_BLOCK = 0, 1, 2
 
 EXPORTS = ["moe_select_experts", "moe_workspace_bytes", "moe_pre_reorder_quant",
-           "moe_grouped_gemm_fp8", "moe_act_requant", "moe_post_reorder", "moe_status_string"]
+           "moe_grouped_gemm_fp8", "moe_act_requant", "moe_post_reorder", "moe_status_string",
+           "moe_router_select"]
 
 _lib = None
 
@@ -68,6 +69,9 @@ def load_library():
     lib.moe_act_requant.argtypes = [P, P, I32, I64, I32, I32, P, P, I64, P, SZ, P]
     lib.moe_post_reorder.restype = ctypes.c_int
     lib.moe_post_reorder.argtypes = [P, P, P, I64, I32, I32, I64, P, P]
+    lib.moe_router_select.restype = ctypes.c_int
+    lib.moe_router_select.argtypes = [P, P, P, I64, I32, I32, I32, I32, I32, I32, I32, F32, I32, P, P,
+                                      P, P]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -129,6 +133,28 @@ def moe_select_experts(logits, correction_bias, topk_ids, topk_weights, *, topk,
         renormalize, float(routed_scaling_factor), apply_rsf, _ptr(topk_ids), _ptr(topk_weights),
         _stream(stream))
     _check(rc, "moe_select_experts")
+
+
+def moe_router_select(x, wg, correction_bias, logits, topk_ids, topk_weights, *, topk, n_group=1,
+                      topk_group=1, score_fn=SCORE_SOFTMAX, renormalize=1,
+                      routed_scaling_factor=1.0, apply_rsf=1, stream=None):
+    """Router projection logits = x @ wg^T (x bf16 [T, H], wg bf16 [E, H]) into
+    `logits` (fp32 [T, E]), then stage 1 on them."""
+    _dtype(x, torch.bfloat16, name="x")
+    _dtype(wg, torch.bfloat16, name="wg")
+    _dtype(correction_bias, torch.float32, name="correction_bias")
+    _dtype(logits, torch.float32, name="logits")
+    _dtype(topk_ids, torch.int32, name="topk_ids")
+    _dtype(topk_weights, torch.float32, name="topk_weights")
+    T, H = x.shape
+    E = wg.shape[0]
+    if wg.shape[1] != H or tuple(logits.shape) != (T, E):
+        raise MoEError("moe_router_select: shapes of x, wg and logits disagree")
+    rc = load_library().moe_router_select(
+        _ptr(x), _ptr(wg), _ptr(correction_bias), T, H, E, topk, n_group, topk_group, score_fn,
+        renormalize, float(routed_scaling_factor), apply_rsf, _ptr(logits), _ptr(topk_ids),
+        _ptr(topk_weights), _stream(stream))
+    _check(rc, "moe_router_select")
 
 
 def moe_pre_reorder_quant(x, topk_ids, a_q, a_scale, src2dst, dst2src, seg_indptr, workspace, *,

@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 
-SOURCES = ["abi.hip", "select_experts.hip", "pre_reorder.hip", "grouped_gemm.hip",
+SOURCES = ["abi.hip", "select_experts.hip", "router.hip", "pre_reorder.hip", "grouped_gemm.hip",
            "act_requant.hip", "post_reorder.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -23,6 +23,12 @@ static inline int launch_status() {
 
 int device_cu_count();  // compute units of the current device (cached per device)
 
+// select_experts.hip: argument checks + launch of stage 1 on given logits
+int launch_select_experts(const float* logits, const float* correction_bias, int64_t T, int32_t E,
+                          int32_t topk, int32_t n_group, int32_t topk_group, int32_t score_fn,
+                          int32_t renormalize, float routed_scaling_factor, int32_t apply_rsf,
+                          int32_t* topk_ids, float* topk_weights, hipStream_t s);
+
 static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ---- exact-math helpers (the fp32 operation sequence is part of the contract) --

@@ -197,12 +197,14 @@ __global__ __launch_bounds__(256) void select_experts_kernel(
 }  // namespace
 }  // namespace moe
 
-extern "C" int moe_select_experts(const float* logits, const float* correction_bias, int64_t T,
-                                  int32_t E, int32_t topk, int32_t n_group, int32_t topk_group,
-                                  int32_t score_fn, int32_t renormalize,
-                                  float routed_scaling_factor, int32_t apply_rsf,
-                                  int32_t* topk_ids, float* topk_weights, void* stream) {
-    using namespace moe;
+namespace moe {
+
+// Argument checks and launch of the select kernel (shared by moe_select_experts
+// and moe_router_select).
+int launch_select_experts(const float* logits, const float* correction_bias, int64_t T, int32_t E,
+                          int32_t topk, int32_t n_group, int32_t topk_group, int32_t score_fn,
+                          int32_t renormalize, float routed_scaling_factor, int32_t apply_rsf,
+                          int32_t* topk_ids, float* topk_weights, hipStream_t s) {
     if (T < 0 || E <= 0 || topk <= 0 || n_group <= 0 || topk_group <= 0) return MOE_ERR_INVALID_ARG;
     if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
     if (E > 512 || topk > 32 || topk > E || n_group > 64) return MOE_ERR_UNSUPPORTED;
@@ -215,7 +217,6 @@ extern "C" int moe_select_experts(const float* logits, const float* correction_b
         return MOE_ERR_INVALID_ARG;
     (void)hipGetLastError();
     const dim3 grid((unsigned)ceil_div(T, kTokensPerBlock)), block(256);
-    hipStream_t s = (hipStream_t)stream;
 #define MOE_LAUNCH_SELECT(EPL)                                                                     \
     hipLaunchKernelGGL(select_experts_kernel<EPL>, grid, block, 0, s, logits, correction_bias, T, \
                        E, topk, n_group, topk_group, score_fn, renormalize,                      \
@@ -226,4 +227,16 @@ extern "C" int moe_select_experts(const float* logits, const float* correction_b
     else MOE_LAUNCH_SELECT(8);
 #undef MOE_LAUNCH_SELECT
     return launch_status();
+}
+
+}  // namespace moe
+
+extern "C" int moe_select_experts(const float* logits, const float* correction_bias, int64_t T,
+                                  int32_t E, int32_t topk, int32_t n_group, int32_t topk_group,
+                                  int32_t score_fn, int32_t renormalize,
+                                  float routed_scaling_factor, int32_t apply_rsf,
+                                  int32_t* topk_ids, float* topk_weights, void* stream) {
+    return moe::launch_select_experts(logits, correction_bias, T, E, topk, n_group, topk_group,
+                                      score_fn, renormalize, routed_scaling_factor, apply_rsf,
+                                      topk_ids, topk_weights, (hipStream_t)stream);
 }

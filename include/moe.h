@@ -9,6 +9,8 @@
  *                          activation scale indexed by row
  *   moe_act_requant        SiLU(gate) * up, then dynamic FP8 requantisation
  *   moe_post_reorder       top-k weighted combine back to token order
+ * and one extension before stage 1:
+ *   moe_router_select      router projection (bf16 MFMA) + stage 1
  *
  * Conventions shared by every call
  *   - C linkage; all tensors are device pointers to caller-owned memory,
@@ -91,6 +93,26 @@ int moe_select_experts(const float* logits, const float* correction_bias, int64_
                        int32_t topk, int32_t n_group, int32_t topk_group, int32_t score_fn,
                        int32_t renormalize, float routed_scaling_factor, int32_t apply_rsf,
                        int32_t* topk_ids, float* topk_weights, void* stream);
+
+/*
+ * Router projection + stage 1 (extension: the gate from hidden states).
+ * Source: the fused gate of "[1/2] sgl-kernel: Fuse routed scaling factor into
+ * select_experts" (sglang PR #8364), Motivation: the gate scores the router's
+ * logits; this call computes those logits first.
+ *
+ *   logits[t, e] = sum_h x[t, h] * wg[e, h], fp32 accumulation of the bf16
+ *   products (summation order of the matrix cores), written to `logits`, then
+ *   moe_select_experts on them with the same stage-1 arguments.
+ *   x_bf16   bf16 [T, H];  wg_bf16  bf16 [E, H] (one row per expert, the
+ *            transpose of the [H, E] projection);  logits  fp32 [T, E] out.
+ * Limits: H % 8 == 0, E % 4 == 0, and those of moe_select_experts. A stage-1
+ * argument error is reported before anything is enqueued.
+ */
+int moe_router_select(const void* x_bf16, const void* wg_bf16, const float* correction_bias,
+                      int64_t T, int32_t H, int32_t E, int32_t topk, int32_t n_group,
+                      int32_t topk_group, int32_t score_fn, int32_t renormalize,
+                      float routed_scaling_factor, int32_t apply_rsf, float* logits,
+                      int32_t* topk_ids, float* topk_weights, void* stream);
 
 /* Bytes of device workspace that moe_pre_reorder_quant and moe_act_requant
  * need for these sizes (the same buffer may serve both calls in turn). */

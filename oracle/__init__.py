@@ -61,6 +61,8 @@ def _load():
     lib.oracle_grouped_gemm_rows.argtypes = [P, P, I32, P, P, I32, P, I32, I32, I32, P, I64, P]
     lib.oracle_act_requant.restype = ctypes.c_int
     lib.oracle_act_requant.argtypes = [P, P, I32, I32, I32, P, P]
+    lib.oracle_router_logits.restype = ctypes.c_int
+    lib.oracle_router_logits.argtypes = [P, P, I64, I32, I32, P]
     lib.oracle_post_reorder.restype = ctypes.c_int
     lib.oracle_post_reorder.argtypes = [P, P, P, I64, I32, I32, P]
     lib.oracle_dense_layer.restype = ctypes.c_int
@@ -225,6 +227,19 @@ def act_requant(gateup_bits, seg_indptr, act_quant):
                                     _p(a_scale))
     _check(rc, "act_requant")
     return a_q, a_scale
+
+
+def router_logits(x_bits, wg_bits):
+    """Router projection: fp32 [T, E] = fp32(sum_h x[t,h] * wg[e,h]) of bf16 x [T, H], wg [E, H]."""
+    x = _c(x_bits, np.uint16)
+    wg = _c(wg_bits, np.uint16)
+    T, H = x.shape
+    E, H2 = wg.shape
+    assert H == H2
+    out = np.empty((T, E), dtype=np.float32)
+    rc = _load().oracle_router_logits(_p(x), _p(wg), T, H, E, _p(out))
+    _check(rc, "router_logits")
+    return out
 
 
 def post_reorder(down_bits, src2dst, weights, T, topk):

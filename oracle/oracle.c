@@ -21,6 +21,7 @@
  *     summary for layer.py (sglang_per_token_quant_fp8 after the activation).
  *   - top-k weighted combine: PR #8364 Motivation (moe_sum_reduce is the
  *     final weighted sum over the selected experts).
+ *   - router projection (logits the gate scores): PR #8364 Motivation.
  *
  * Precision: the GEMM accumulates in fp32 over dequantised FP8 operands. Every
  * step whose floating-point result decides an integer (expert ids, FP8 codes)
@@ -571,6 +572,30 @@ int oracle_post_reorder(const uint16_t* down, const int32_t* src2dst, const floa
                 acc += (double)w[t * topk + j] * (double)oracle_bf16_to_f32(down[(int64_t)r * H + h]);
             }
             out[t * H + h] = oracle_bf16_rne_f64(acc);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Router projection (the gate's input)                                       */
+/* ------------------------------------------------------------------------- */
+
+/* logits[t, e] = fp32( sum_h x[t, h] * wg[e, h] ) with x, wg bf16. Every product
+ * of two bf16 values is exact in fp64 and the fp64 sum over h (ascending) is
+ * exact to far below fp32 resolution for the sizes here, so this is the
+ * correctly rounded fp32 value of the exact dot product, up to fp64 rounding.
+ * The pages' fused gate scores these logits ("[1/2] sgl-kernel: Fuse routed
+ * scaling factor into select_experts", sglang PR #8364, Motivation). */
+int oracle_router_logits(const uint16_t* x, const uint16_t* wg, int64_t T, int H, int E,
+                         float* logits) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h)
+                acc += (double)oracle_bf16_to_f32(x[t * H + h]) * (double)oracle_bf16_to_f32(wg[(int64_t)e * H + h]);
+            logits[t * E + e] = (float)acc;
         }
     }
     return 0;

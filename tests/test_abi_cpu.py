@@ -148,3 +148,21 @@ def test_binding_keyword_only():
     assert sig.parameters["act_quant"].kind == inspect.Parameter.KEYWORD_ONLY
     sig = inspect.signature(moe.moe_select_experts)
     assert sig.parameters["topk"].kind == inspect.Parameter.KEYWORD_ONLY
+
+
+def test_router_select_rejects(lib):
+    f = lib.moe_router_select
+    def call(T=4, H=64, E=8, k=2, ng=1, tg=1, sf=0, x=FAKE, wg=FAKE, logits=FAKE, ids=FAKE):
+        return f(x, wg, None, T, H, E, k, ng, tg, sf, 1, 1.0, 1, logits, ids, FAKE, None)
+    assert call(H=12) == moe.MOE_ERR_UNSUPPORTED          # H % 8
+    assert call(E=6) == moe.MOE_ERR_UNSUPPORTED           # E % 4
+    assert call(E=0) == moe.MOE_ERR_INVALID_ARG
+    assert call(T=-1) == moe.MOE_ERR_INVALID_ARG
+    assert call(x=None) == moe.MOE_ERR_NULL
+    assert call(wg=None) == moe.MOE_ERR_NULL
+    assert call(logits=None) == moe.MOE_ERR_NULL
+    assert call(x=ctypes.c_void_p(0x10008)) == moe.MOE_ERR_INVALID_ARG   # misaligned
+    assert call(k=9) == moe.MOE_ERR_UNSUPPORTED           # stage-1 limits, checked first
+    assert call(ng=3, sf=1) == moe.MOE_ERR_INVALID_ARG
+    assert call(ids=None) == moe.MOE_ERR_NULL
+    assert call(T=0) == moe.MOE_OK

@@ -138,6 +138,12 @@ def gen_router(cfg: MoEConfig, seed: int = 0) -> np.ndarray:
             * np.float32(0.02))
 
 
+def gen_router_bf16(cfg: MoEConfig, seed: int = 0) -> np.ndarray:
+    """The router weight W_g of gen_router rounded to bf16 and stored one row per
+    expert: uint16 bits of shape [E, H] (the layout the GPU router reads)."""
+    return np.ascontiguousarray(to_bf16_bits(gen_router(cfg, seed)).T)
+
+
 def gen_bias(cfg: MoEConfig, seed: int = 0) -> Optional[np.ndarray]:
     """Per-expert correction bias ~ N(0, 0.01) [E], or None when the workload has none."""
     if not cfg.use_bias:
