@@ -49,11 +49,11 @@ def parse():
 
 def algorithmic_work(cfg, seg, a_scale_bytes13, a_scale_bytes2, w13_scale_numel, w2_scale_numel):
     """Bytes each stage must move (inputs read once, outputs written once) and GEMM FLOPs."""
-    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.slots
     M = int(seg[-1])
     counts = np.diff(seg)
     nonempty = int((counts > 0).sum())
-    El = cfg.num_local
+    El = cfg.local_experts
     b13 = nonempty * 2 * I * H + w13_scale_numel * 4 * nonempty // max(El, 1)
     b2 = nonempty * H * I + w2_scale_numel * 4 * nonempty // max(El, 1)
     tok_local = None
@@ -102,7 +102,8 @@ def main():
     bias = up(inp.bias) if inp.bias is not None else None
     w13, s13 = up(inp.w13), up(inp.w13_scale.reshape(-1))
     w2, s2 = up(inp.w2), up(inp.w2_scale.reshape(-1))
-    buf = moe.LayerBuffers.allocate(cfg.T, cfg.H, cfg.I, cfg.topk, cfg.num_local, cfg.act_quant)
+    buf = moe.LayerBuffers.allocate(cfg.T, cfg.H, cfg.I, cfg.topk, cfg.num_local, cfg.act_quant,
+                                    n_shared=cfg.n_shared)
     gen_s = time.time() - t0
     print(f"[bench] {cfg.name}: inputs ready in {gen_s:.1f}s", file=sys.stderr, flush=True)
 
@@ -118,15 +119,30 @@ def main():
             if events is not None:
                 events[i].record()
         mark(0)
-        moe.moe_select_experts(logits, bias, buf.topk_ids, buf.topk_weights, topk=cfg.topk,
-                               n_group=cfg.n_group, topk_group=cfg.topk_group,
-                               score_fn=cfg.score_fn, renormalize=cfg.renormalize,
-                               routed_scaling_factor=cfg.rsf, apply_rsf=cfg.apply_rsf)
+        if cfg.n_shared:
+            moe.moe_select_experts_shared(logits, bias, buf.topk_ids, buf.topk_weights,
+                                          topk=cfg.topk, n_shared=cfg.n_shared,
+                                          shared_weight=cfg.shared_weight, n_group=cfg.n_group,
+                                          topk_group=cfg.topk_group, score_fn=cfg.score_fn,
+                                          renormalize=cfg.renormalize,
+                                          routed_scaling_factor=cfg.rsf, apply_rsf=cfg.apply_rsf)
+        else:
+            moe.moe_select_experts(logits, bias, buf.topk_ids, buf.topk_weights, topk=cfg.topk,
+                                   n_group=cfg.n_group, topk_group=cfg.topk_group,
+                                   score_fn=cfg.score_fn, renormalize=cfg.renormalize,
+                                   routed_scaling_factor=cfg.rsf, apply_rsf=cfg.apply_rsf)
         mark(1)
-        moe.moe_pre_reorder_quant(x, buf.topk_ids, buf.a13, buf.a13_scale, buf.src2dst,
-                                  buf.dst2src, buf.seg_indptr, buf.workspace,
-                                  expert_start=cfg.expert_start, num_local=cfg.num_local,
-                                  act_quant=cfg.act_quant)
+        if cfg.n_shared:
+            moe.moe_pre_reorder_quant_shared(x, buf.topk_ids, buf.a13, buf.a13_scale, buf.src2dst,
+                                             buf.dst2src, buf.seg_indptr, buf.workspace,
+                                             expert_start=cfg.expert_start, num_routed=cfg.num_local,
+                                             shared_base=cfg.E, n_shared=cfg.n_shared,
+                                             act_quant=cfg.act_quant)
+        else:
+            moe.moe_pre_reorder_quant(x, buf.topk_ids, buf.a13, buf.a13_scale, buf.src2dst,
+                                      buf.dst2src, buf.seg_indptr, buf.workspace,
+                                      expert_start=cfg.expert_start, num_local=cfg.num_local,
+                                      act_quant=cfg.act_quant)
         mark(2)
         moe.moe_grouped_gemm_fp8(buf.a13, buf.a13_scale, w13, s13, buf.seg_indptr, buf.c13,
                                  act_quant=cfg.act_quant, w_quant=cfg.w_quant)
@@ -197,7 +213,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
-                   "topk": cfg.topk, "num_local": cfg.num_local, "M": M,
+                   "topk": cfg.topk, "num_local": cfg.num_local, "n_shared": cfg.n_shared, "M": M,
                    "experts_with_rows": nonempty, "act_quant": cfg.act_quant,
                    "w_quant": cfg.w_quant, "parallelism": "single GPU (one EP share)"},
         "roofline": roof, "gemm": gemm, "stages": stage_stats,

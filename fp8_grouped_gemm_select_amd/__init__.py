@@ -31,7 +31,7 @@ W_PER_EXPERT, W_PER_CHANNEL, W_BLOCK = 0, 1, 2
 
 EXPORTS = ["moe_select_experts", "moe_workspace_bytes", "moe_pre_reorder_quant",
            "moe_grouped_gemm_fp8", "moe_act_requant", "moe_post_reorder", "moe_status_string",
-           "moe_router_select"]
+           "moe_router_select", "moe_select_experts_shared", "moe_pre_reorder_quant_shared"]
 
 _lib = None
 
@@ -69,6 +69,12 @@ def load_library():
     lib.moe_act_requant.argtypes = [P, P, I32, I64, I32, I32, P, P, I64, P, SZ, P]
     lib.moe_post_reorder.restype = ctypes.c_int
     lib.moe_post_reorder.argtypes = [P, P, P, I64, I32, I32, I64, P, P]
+    lib.moe_select_experts_shared.restype = ctypes.c_int
+    lib.moe_select_experts_shared.argtypes = [P, P, I64, I32, I32, I32, I32, I32, I32, F32, I32, I32,
+                                              F32, P, P, P]
+    lib.moe_pre_reorder_quant_shared.restype = ctypes.c_int
+    lib.moe_pre_reorder_quant_shared.argtypes = [P, P, I64, I32, I32, I32, I32, I32, I32, I32, I64, P,
+                                                 P, I64, P, P, P, P, SZ, P]
     lib.moe_router_select.restype = ctypes.c_int
     lib.moe_router_select.argtypes = [P, P, P, I64, I32, I32, I32, I32, I32, I32, I32, F32, I32, P, P,
                                       P, P]
@@ -155,6 +161,45 @@ def moe_router_select(x, wg, correction_bias, logits, topk_ids, topk_weights, *,
         renormalize, float(routed_scaling_factor), apply_rsf, _ptr(logits), _ptr(topk_ids),
         _ptr(topk_weights), _stream(stream))
     _check(rc, "moe_router_select")
+
+
+def moe_select_experts_shared(logits, correction_bias, topk_ids, topk_weights, *, topk, n_shared,
+                              shared_weight, n_group=1, topk_group=1, score_fn=SCORE_SOFTMAX,
+                              renormalize=1, routed_scaling_factor=1.0, apply_rsf=1, stream=None):
+    """Stage 1 plus n_shared always-selected slots per token (ids E.., weight
+    shared_weight): topk_ids / topk_weights are [T, topk + n_shared]."""
+    _dtype(logits, torch.float32, name="logits")
+    _dtype(correction_bias, torch.float32, name="correction_bias")
+    _dtype(topk_ids, torch.int32, name="topk_ids")
+    _dtype(topk_weights, torch.float32, name="topk_weights")
+    T, E = logits.shape
+    if topk_ids.shape[1] != topk + n_shared or topk_weights.shape[1] != topk + n_shared:
+        raise MoEError("moe_select_experts_shared: outputs need topk + n_shared columns")
+    rc = load_library().moe_select_experts_shared(
+        _ptr(logits), _ptr(correction_bias), T, E, topk, n_group, topk_group, score_fn,
+        renormalize, float(routed_scaling_factor), apply_rsf, n_shared, float(shared_weight),
+        _ptr(topk_ids), _ptr(topk_weights), _stream(stream))
+    _check(rc, "moe_select_experts_shared")
+
+
+def moe_pre_reorder_quant_shared(x, topk_ids, a_q, a_scale, src2dst, dst2src, seg_indptr, workspace,
+                                 *, expert_start, num_routed, shared_base, n_shared, act_quant,
+                                 stream=None):
+    """Stage 2 with shared experts: ids in [shared_base, shared_base + n_shared) are
+    local experts num_routed.. (seg_indptr has num_routed + n_shared + 1 entries)."""
+    _dtype(x, torch.bfloat16, name="x")
+    _dtype(topk_ids, torch.int32, name="topk_ids")
+    _dtype(a_q, torch.uint8, torch.float8_e4m3fn, name="a_q")
+    _dtype(a_scale, torch.float32, name="a_scale")
+    T, H = x.shape
+    topk = topk_ids.shape[1]
+    m_cap = a_q.shape[0]
+    rc = load_library().moe_pre_reorder_quant_shared(
+        _ptr(x), _ptr(topk_ids), T, H, topk, expert_start, num_routed, shared_base, n_shared,
+        act_quant, m_cap, _ptr(a_q), _ptr(a_scale), a_scale.numel(), _ptr(src2dst), _ptr(dst2src),
+        _ptr(seg_indptr), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(rc, "moe_pre_reorder_quant_shared")
 
 
 def moe_pre_reorder_quant(x, topk_ids, a_q, a_scale, src2dst, dst2src, seg_indptr, workspace, *,

@@ -27,7 +27,8 @@ int device_cu_count();  // compute units of the current device (cached per devic
 int launch_select_experts(const float* logits, const float* correction_bias, int64_t T, int32_t E,
                           int32_t topk, int32_t n_group, int32_t topk_group, int32_t score_fn,
                           int32_t renormalize, float routed_scaling_factor, int32_t apply_rsf,
-                          int32_t* topk_ids, float* topk_weights, hipStream_t s);
+                          int32_t* topk_ids, float* topk_weights, hipStream_t s, int32_t n_shared,
+                          float shared_weight);
 
 static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -67,6 +67,20 @@ inline PreWs pre_ws_carve(void* ws, int64_t T, int32_t topk, int32_t num_local) 
     return w;
 }
 
+// Local expert index of a global id: the routed local range [expert_start,
+// expert_start + num_routed) maps to 0.., the shared ids [shared_base,
+// shared_base + n_shared) to num_routed.., anything else is not local (-1).
+struct LocalMap {
+    int expert_start, num_routed, shared_base, n_shared;
+};
+__device__ __forceinline__ int local_of(int id, const LocalMap& m) {
+    const int r = id - m.expert_start;
+    if (r >= 0 && r < m.num_routed) return r;
+    const int q = id - m.shared_base;
+    if (q >= 0 && q < m.n_shared) return m.num_routed + q;
+    return -1;
+}
+
 // ---- count: chunk-local stable ranks -----------------------------------------
 // One 64-thread block per chunk of 64 pairs; lane l holds pair 64 c + l. Its
 // rank is the number of lower lanes holding the same local expert (compared
@@ -74,7 +88,7 @@ inline PreWs pre_ws_carve(void* ws, int64_t T, int32_t topk, int32_t num_local) 
 // occurrence in the chunk records the count. cnt[] (dynamic LDS, num_local
 // ints) gives every (expert, chunk) entry exactly one writer.
 __global__ __launch_bounds__(64) void pr_count_kernel(const int32_t* __restrict__ ids, int64_t F,
-                                                      int expert_start, int num_local, int64_t nch,
+                                                      LocalMap map, int num_local, int64_t nch,
                                                       int32_t* __restrict__ src2dst,
                                                       int32_t* __restrict__ counts) {
     extern __shared__ int32_t cnt[];
@@ -82,9 +96,8 @@ __global__ __launch_bounds__(64) void pr_count_kernel(const int32_t* __restrict_
     const int64_t chunk = blockIdx.x;
     for (int e = lane; e < num_local; e += 64) cnt[e] = 0;
     const int64_t f = chunk * kChunkPairs + lane;
-    const int ev = f < F ? ids[f] - expert_start : -1;
-    const bool local = ev >= 0 && ev < num_local;
-    const int e = local ? ev : -1;
+    const int e = f < F ? local_of(ids[f], map) : -1;
+    const bool local = e >= 0;
     int below = 0, all = 0;
 #pragma unroll
     for (int j = 0; j < 64; ++j) {
@@ -205,15 +218,12 @@ __device__ __forceinline__ uint4 quant16(const uint4& a, const uint4& b, float i
 template <int MODE>
 __device__ __forceinline__ void scatter_token(
     const uint4* __restrict__ x, const int32_t* __restrict__ ids, int64_t t, int H, int topk,
-    int expert_start, int num_local, int64_t nch, const int32_t* __restrict__ offs,
+    const LocalMap& map, int64_t nch, const int32_t* __restrict__ offs,
     int32_t* __restrict__ src2dst, int32_t* __restrict__ dst2src, uint8_t* __restrict__ a_q,
     float* __restrict__ a_scale, const float* __restrict__ tscale, int64_t m_cap, int lane) {
     const int64_t f = t * topk + lane;
     int e = -1;
-    if (lane < topk) {
-        const int ev = ids[f] - expert_start;
-        if (ev >= 0 && ev < num_local) e = ev;
-    }
+    if (lane < topk) e = local_of(ids[f], map);
     if (__ballot(e >= 0) == 0) {
         if (lane < topk) src2dst[f] = -1;
         return;
@@ -328,7 +338,7 @@ __device__ __forceinline__ void scatter_token(
 template <int MODE>
 __global__ __launch_bounds__(256) void pr_scatter_quant_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ ids, int64_t T, int H, int topk,
-    int expert_start, int num_local, int64_t nch, const int32_t* __restrict__ offs,
+    LocalMap map, int num_local, int64_t nch, const int32_t* __restrict__ offs,
     const int32_t* __restrict__ seg, int32_t* __restrict__ src2dst, int32_t* __restrict__ dst2src,
     uint8_t* __restrict__ a_q, float* __restrict__ a_scale, const float* __restrict__ tscale,
     int64_t m_cap) {
@@ -336,7 +346,7 @@ __global__ __launch_bounds__(256) void pr_scatter_quant_kernel(
     const int64_t t = (int64_t)blockIdx.x * 4 + wid;
     const int64_t M = seg[num_local];  // needed only for the tail below
     if (t < T)
-        scatter_token<MODE>(x, ids, t, H, topk, expert_start, num_local, nch, offs, src2dst, dst2src,
+        scatter_token<MODE>(x, ids, t, H, topk, map, nch, offs, src2dst, dst2src,
                             a_q, a_scale, tscale, m_cap, lane);
     // rows M .. m_cap-1 of dst2src are -1 (grid-stride over the whole grid)
     for (int64_t r = M + (int64_t)blockIdx.x * 256 + threadIdx.x; r < m_cap; r += (int64_t)gridDim.x * 256)
@@ -351,13 +361,21 @@ size_t pre_reorder_ws_bytes(int64_t T, int32_t topk, int32_t num_local) {
 
 }  // namespace moe
 
-extern "C" int moe_pre_reorder_quant(const void* x_bf16, const int32_t* topk_ids, int64_t T,
-                                     int32_t H, int32_t topk, int32_t expert_start,
-                                     int32_t num_local, int32_t act_quant, int64_t m_cap,
-                                     uint8_t* a_q, float* a_scale, int64_t a_scale_numel,
-                                     int32_t* src2dst, int32_t* dst2src, int32_t* seg_indptr,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
-    using namespace moe;
+namespace moe {
+// Shared by moe_pre_reorder_quant (no shared experts) and
+// moe_pre_reorder_quant_shared; num_local = num_routed + n_shared local experts.
+static int pre_reorder_impl(const void* x_bf16, const int32_t* topk_ids, int64_t T, int32_t H,
+                            int32_t topk, int32_t expert_start, int32_t num_routed,
+                            int32_t shared_base, int32_t n_shared, int32_t act_quant, int64_t m_cap,
+                            uint8_t* a_q, float* a_scale, int64_t a_scale_numel, int32_t* src2dst,
+                            int32_t* dst2src, int32_t* seg_indptr, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    if (num_routed < 0 || n_shared < 0 || n_shared > 64 || shared_base < 0) return MOE_ERR_INVALID_ARG;
+    if (n_shared > 0 && (int64_t)shared_base < (int64_t)expert_start + num_routed &&
+        (int64_t)shared_base + n_shared > expert_start)
+        return MOE_ERR_INVALID_ARG;  // shared ids must not overlap the routed local range
+    const int32_t num_local = num_routed + n_shared;
+    const LocalMap map{expert_start, num_routed, shared_base, n_shared};
     if (T < 0 || H <= 0 || topk <= 0 || num_local < 0 || m_cap < 0) return MOE_ERR_INVALID_ARG;
     if (act_quant < MOE_ACT_PER_TENSOR || act_quant > MOE_ACT_PER_GROUP) return MOE_ERR_INVALID_ARG;
     if (H % 16 != 0 || topk > 32 || num_local > 8192) return MOE_ERR_UNSUPPORTED;
@@ -384,7 +402,7 @@ extern "C" int moe_pre_reorder_quant(const void* x_bf16, const int32_t* topk_ids
     PreWs ws = pre_ws_carve(workspace, T, topk, num_local);
     if (nch > 0 && num_local > 0)
         hipLaunchKernelGGL(pr_count_kernel, dim3((unsigned)nch), dim3(64),
-                           sizeof(int32_t) * num_local, s, topk_ids, T * (int64_t)topk, expert_start,
+                           sizeof(int32_t) * num_local, s, topk_ids, T * (int64_t)topk, map,
                            num_local, nch, src2dst, ws.counts);
     const int per_tensor = act_quant == MOE_ACT_PER_TENSOR;
     const int64_t n16 = T * (int64_t)H / 16;
@@ -401,7 +419,7 @@ extern "C" int moe_pre_reorder_quant(const void* x_bf16, const int32_t* topk_ids
     if (m_cap > 0 || T > 0) {
 #define MOE_LAUNCH_SCATTER(MODE)                                                                  \
     hipLaunchKernelGGL(pr_scatter_quant_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s,     \
-                       (const uint4*)x_bf16, topk_ids, T, H, topk, expert_start, num_local, nch, \
+                       (const uint4*)x_bf16, topk_ids, T, H, topk, map, num_local, nch,          \
                        ws.offs, seg_indptr, src2dst, dst2src, a_q, a_scale, ws.tscale, m_cap)
         if (act_quant == MOE_ACT_PER_TENSOR) MOE_LAUNCH_SCATTER(MOE_ACT_PER_TENSOR);
         else if (act_quant == MOE_ACT_PER_TOKEN) MOE_LAUNCH_SCATTER(MOE_ACT_PER_TOKEN);
@@ -409,4 +427,28 @@ extern "C" int moe_pre_reorder_quant(const void* x_bf16, const int32_t* topk_ids
 #undef MOE_LAUNCH_SCATTER
     }
     return launch_status();
+}
+}  // namespace moe
+
+extern "C" int moe_pre_reorder_quant(const void* x_bf16, const int32_t* topk_ids, int64_t T,
+                                     int32_t H, int32_t topk, int32_t expert_start,
+                                     int32_t num_local, int32_t act_quant, int64_t m_cap,
+                                     uint8_t* a_q, float* a_scale, int64_t a_scale_numel,
+                                     int32_t* src2dst, int32_t* dst2src, int32_t* seg_indptr,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    return moe::pre_reorder_impl(x_bf16, topk_ids, T, H, topk, expert_start, num_local, 0, 0,
+                                 act_quant, m_cap, a_q, a_scale, a_scale_numel, src2dst, dst2src,
+                                 seg_indptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" int moe_pre_reorder_quant_shared(const void* x_bf16, const int32_t* topk_ids, int64_t T,
+                                            int32_t H, int32_t topk, int32_t expert_start,
+                                            int32_t num_routed, int32_t shared_base,
+                                            int32_t n_shared, int32_t act_quant, int64_t m_cap,
+                                            uint8_t* a_q, float* a_scale, int64_t a_scale_numel,
+                                            int32_t* src2dst, int32_t* dst2src, int32_t* seg_indptr,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+    return moe::pre_reorder_impl(x_bf16, topk_ids, T, H, topk, expert_start, num_routed, shared_base,
+                                 n_shared, act_quant, m_cap, a_q, a_scale, a_scale_numel, src2dst,
+                                 dst2src, seg_indptr, workspace, workspace_bytes, stream);
 }

@@ -121,7 +121,7 @@ extern "C" int moe_router_select(const void* x_bf16, const void* wg_bf16, const 
         (score_fn == MOE_SCORE_SOFTMAX && (correction_bias || n_group > 1)))
         return launch_select_experts(logits, correction_bias, T, E, topk, n_group, topk_group, score_fn,
                                      renormalize, routed_scaling_factor, apply_rsf, topk_ids,
-                                     topk_weights, (hipStream_t)stream);  // returns the precise error
+                                     topk_weights, (hipStream_t)stream, 0, 0.0f);  // returns the precise error
     if (!topk_ids || !topk_weights) return MOE_ERR_NULL;
     if (!aligned16(topk_ids) || !aligned16(topk_weights)) return MOE_ERR_INVALID_ARG;
     (void)hipGetLastError();
@@ -132,5 +132,6 @@ extern "C" int moe_router_select(const void* x_bf16, const void* wg_bf16, const 
     const int st = launch_status();
     if (st != MOE_OK) return st;
     return launch_select_experts(logits, correction_bias, T, E, topk, n_group, topk_group, score_fn,
-                                 renormalize, routed_scaling_factor, apply_rsf, topk_ids, topk_weights, s);
+                                 renormalize, routed_scaling_factor, apply_rsf, topk_ids, topk_weights, s,
+                                 0, 0.0f);
 }

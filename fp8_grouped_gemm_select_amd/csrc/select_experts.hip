@@ -57,7 +57,8 @@ template <int EPL>
 __global__ __launch_bounds__(256) void select_experts_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int E, int topk,
     int n_group, int topk_group, int score_fn, int renormalize, float rsf, int apply_rsf,
-    int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+    int n_shared, float shared_weight, int stride, int32_t* __restrict__ ids_out,
+    float* __restrict__ w_out) {
     __shared__ float s_key[kTokensPerBlock][EPL * 64];
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * kTokensPerBlock + wid;
@@ -189,8 +190,11 @@ __global__ __launch_bounds__(256) void select_experts_kernel(
     float w = v / (renormalize ? sel : all);
     if (apply_rsf) w = w * rsf;
     if (active && lane < topk) {
-        ids_out[t * topk + lane] = my_id;
-        w_out[t * topk + lane] = w;
+        ids_out[t * stride + lane] = my_id;
+        w_out[t * stride + lane] = w;
+    } else if (active && lane < topk + n_shared) {  // shared experts: ids E.., fixed weight
+        ids_out[t * stride + lane] = E + (lane - topk);
+        w_out[t * stride + lane] = shared_weight;
     }
 }
 
@@ -204,8 +208,10 @@ namespace moe {
 int launch_select_experts(const float* logits, const float* correction_bias, int64_t T, int32_t E,
                           int32_t topk, int32_t n_group, int32_t topk_group, int32_t score_fn,
                           int32_t renormalize, float routed_scaling_factor, int32_t apply_rsf,
-                          int32_t* topk_ids, float* topk_weights, hipStream_t s) {
+                          int32_t* topk_ids, float* topk_weights, hipStream_t s, int32_t n_shared,
+                          float shared_weight) {
     if (T < 0 || E <= 0 || topk <= 0 || n_group <= 0 || topk_group <= 0) return MOE_ERR_INVALID_ARG;
+    if (n_shared < 0 || topk + n_shared > 64) return n_shared < 0 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED;
     if (score_fn != MOE_SCORE_SOFTMAX && score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
     if (E > 512 || topk > 32 || topk > E || n_group > 64) return MOE_ERR_UNSUPPORTED;
     if (E % n_group != 0 || topk_group > n_group) return MOE_ERR_INVALID_ARG;
@@ -220,7 +226,8 @@ int launch_select_experts(const float* logits, const float* correction_bias, int
 #define MOE_LAUNCH_SELECT(EPL)                                                                     \
     hipLaunchKernelGGL(select_experts_kernel<EPL>, grid, block, 0, s, logits, correction_bias, T, \
                        E, topk, n_group, topk_group, score_fn, renormalize,                      \
-                       routed_scaling_factor, apply_rsf, topk_ids, topk_weights)
+                       routed_scaling_factor, apply_rsf, n_shared, shared_weight, topk + n_shared, \
+                       topk_ids, topk_weights)
     if (E <= 64) MOE_LAUNCH_SELECT(1);
     else if (E <= 128) MOE_LAUNCH_SELECT(2);
     else if (E <= 256) MOE_LAUNCH_SELECT(4);
@@ -238,5 +245,17 @@ extern "C" int moe_select_experts(const float* logits, const float* correction_b
                                   int32_t* topk_ids, float* topk_weights, void* stream) {
     return moe::launch_select_experts(logits, correction_bias, T, E, topk, n_group, topk_group,
                                       score_fn, renormalize, routed_scaling_factor, apply_rsf,
-                                      topk_ids, topk_weights, (hipStream_t)stream);
+                                      topk_ids, topk_weights, (hipStream_t)stream, 0, 0.0f);
+}
+
+extern "C" int moe_select_experts_shared(const float* logits, const float* correction_bias, int64_t T,
+                                         int32_t E, int32_t topk, int32_t n_group, int32_t topk_group,
+                                         int32_t score_fn, int32_t renormalize,
+                                         float routed_scaling_factor, int32_t apply_rsf,
+                                         int32_t n_shared, float shared_weight, int32_t* topk_ids,
+                                         float* topk_weights, void* stream) {
+    return moe::launch_select_experts(logits, correction_bias, T, E, topk, n_group, topk_group,
+                                      score_fn, renormalize, routed_scaling_factor, apply_rsf,
+                                      topk_ids, topk_weights, (hipStream_t)stream, n_shared,
+                                      shared_weight);
 }

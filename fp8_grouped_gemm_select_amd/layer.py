@@ -13,8 +13,8 @@ import dataclasses
 import torch
 
 from . import (moe_act_requant, moe_grouped_gemm_fp8, moe_post_reorder, moe_pre_reorder_quant,
-               moe_select_experts, moe_workspace_bytes, ACT_PER_GROUP, ACT_PER_TENSOR,
-               ACT_PER_TOKEN)
+               moe_pre_reorder_quant_shared, moe_select_experts, moe_select_experts_shared,
+               moe_workspace_bytes, ACT_PER_GROUP, ACT_PER_TENSOR, ACT_PER_TOKEN)
 
 
 def _scale_numel(act_quant: int, m_cap: int, K: int) -> int:
@@ -42,7 +42,10 @@ class LayerBuffers:
     workspace: torch.Tensor
 
     @staticmethod
-    def allocate(T, H, I, topk, num_local, act_quant, device="cuda"):
+    def allocate(T, H, I, topk, num_local, act_quant, device="cuda", n_shared=0):
+        """Worst-case buffers; with n_shared shared experts every token has
+        topk + n_shared slots over num_local + n_shared local experts."""
+        topk, num_local = topk + n_shared, num_local + n_shared
         m_cap = T * min(topk, num_local)
         dev = torch.device(device)
         ws = moe_workspace_bytes(T, topk, num_local)
@@ -65,15 +68,33 @@ class LayerBuffers:
 
 def layer_forward(x, logits, correction_bias, w13, w13_scale, w2, w2_scale, buf: LayerBuffers, *,
                   topk, n_group, topk_group, score_fn, renormalize, routed_scaling_factor,
-                  apply_rsf, expert_start, num_local, act_quant, w_quant, stream=None):
-    """x bf16 [T,H], logits fp32 [T,E]; w13 e4m3 [E_l,2I,H]; w2 e4m3 [E_l,H,I]. Result in buf.out."""
-    moe_select_experts(logits, correction_bias, buf.topk_ids, buf.topk_weights, topk=topk,
-                       n_group=n_group, topk_group=topk_group, score_fn=score_fn,
-                       renormalize=renormalize, routed_scaling_factor=routed_scaling_factor,
-                       apply_rsf=apply_rsf, stream=stream)
-    moe_pre_reorder_quant(x, buf.topk_ids, buf.a13, buf.a13_scale, buf.src2dst, buf.dst2src,
-                          buf.seg_indptr, buf.workspace, expert_start=expert_start,
-                          num_local=num_local, act_quant=act_quant, stream=stream)
+                  apply_rsf, expert_start, num_local, act_quant, w_quant, n_shared=0,
+                  shared_weight=1.0, stream=None):
+    """x bf16 [T,H], logits fp32 [T,E]; w13 e4m3 [E_l,2I,H]; w2 e4m3 [E_l,H,I]. Result in buf.out.
+
+    With n_shared > 0 the shared experts are the last n_shared entries of w13 /
+    w2 (E_l = num_local + n_shared) and every token also takes them with
+    weight shared_weight, inside the same grouped GEMMs."""
+    if n_shared:
+        moe_select_experts_shared(logits, correction_bias, buf.topk_ids, buf.topk_weights,
+                                  topk=topk, n_shared=n_shared, shared_weight=shared_weight,
+                                  n_group=n_group, topk_group=topk_group, score_fn=score_fn,
+                                  renormalize=renormalize,
+                                  routed_scaling_factor=routed_scaling_factor,
+                                  apply_rsf=apply_rsf, stream=stream)
+        moe_pre_reorder_quant_shared(x, buf.topk_ids, buf.a13, buf.a13_scale, buf.src2dst,
+                                     buf.dst2src, buf.seg_indptr, buf.workspace,
+                                     expert_start=expert_start, num_routed=num_local,
+                                     shared_base=logits.shape[1], n_shared=n_shared,
+                                     act_quant=act_quant, stream=stream)
+    else:
+        moe_select_experts(logits, correction_bias, buf.topk_ids, buf.topk_weights, topk=topk,
+                           n_group=n_group, topk_group=topk_group, score_fn=score_fn,
+                           renormalize=renormalize, routed_scaling_factor=routed_scaling_factor,
+                           apply_rsf=apply_rsf, stream=stream)
+        moe_pre_reorder_quant(x, buf.topk_ids, buf.a13, buf.a13_scale, buf.src2dst, buf.dst2src,
+                              buf.seg_indptr, buf.workspace, expert_start=expert_start,
+                              num_local=num_local, act_quant=act_quant, stream=stream)
     moe_grouped_gemm_fp8(buf.a13, buf.a13_scale, w13, w13_scale, buf.seg_indptr, buf.c13,
                          act_quant=act_quant, w_quant=w_quant, stream=stream)
     moe_act_requant(buf.c13, buf.seg_indptr, buf.a2, buf.a2_scale, buf.workspace,

@@ -9,8 +9,10 @@
  *                          activation scale indexed by row
  *   moe_act_requant        SiLU(gate) * up, then dynamic FP8 requantisation
  *   moe_post_reorder       top-k weighted combine back to token order
- * and one extension before stage 1:
+ * and extensions:
  *   moe_router_select      router projection (bf16 MFMA) + stage 1
+ *   moe_select_experts_shared, moe_pre_reorder_quant_shared
+ *                          shared experts fused as extra local experts
  *
  * Conventions shared by every call
  *   - C linkage; all tensors are device pointers to caller-owned memory,
@@ -113,6 +115,42 @@ int moe_router_select(const void* x_bf16, const void* wg_bf16, const float* corr
                       int32_t topk_group, int32_t score_fn, int32_t renormalize,
                       float routed_scaling_factor, int32_t apply_rsf, float* logits,
                       int32_t* topk_ids, float* topk_weights, void* stream);
+
+/*
+ * Shared-expert fusion (extension). The pages note that shared-expert fusion is
+ * now allowed together with the fused MoE path ("[1/2] sgl-kernel: Fuse routed
+ * scaling factor into select_experts", sglang PR #8364, review summary); the
+ * arithmetic is this library's reading: the n_shared shared experts are extra
+ * slots every token takes, with ids E.. and weight shared_weight, and they run
+ * as local experts num_routed.. inside the same grouped GEMMs (w13 / w2 hold
+ * num_routed + n_shared experts, the shared ones last; every expert has the
+ * same N and K).
+ *
+ * moe_select_experts_shared: moe_select_experts, then slots topk..topk+n_shared-1
+ *   of each token get id E + s and weight shared_weight. topk_ids and
+ *   topk_weights are [T, topk + n_shared]. Limit: topk + n_shared <= 64.
+ */
+int moe_select_experts_shared(const float* logits, const float* correction_bias, int64_t T,
+                              int32_t E, int32_t topk, int32_t n_group, int32_t topk_group,
+                              int32_t score_fn, int32_t renormalize, float routed_scaling_factor,
+                              int32_t apply_rsf, int32_t n_shared, float shared_weight,
+                              int32_t* topk_ids, float* topk_weights, void* stream);
+
+/*
+ * moe_pre_reorder_quant_shared: moe_pre_reorder_quant where ids in
+ *   [expert_start, expert_start + num_routed) are local experts 0..num_routed-1
+ *   and ids in [shared_base, shared_base + n_shared) local experts num_routed..;
+ *   seg_indptr has num_routed + n_shared + 1 entries, m_cap >= T * min(topk,
+ *   num_routed + n_shared) (topk = slots per token, shared ones included), and
+ *   the workspace is moe_workspace_bytes(T, topk, num_routed + n_shared).
+ *   The two id ranges must not overlap (MOE_ERR_INVALID_ARG); 0 <= n_shared <= 64.
+ */
+int moe_pre_reorder_quant_shared(const void* x_bf16, const int32_t* topk_ids, int64_t T, int32_t H,
+                                 int32_t topk, int32_t expert_start, int32_t num_routed,
+                                 int32_t shared_base, int32_t n_shared, int32_t act_quant,
+                                 int64_t m_cap, uint8_t* a_q, float* a_scale, int64_t a_scale_numel,
+                                 int32_t* src2dst, int32_t* dst2src, int32_t* seg_indptr,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace that moe_pre_reorder_quant and moe_act_requant
  * need for these sizes (the same buffer may serve both calls in turn). */

@@ -66,6 +66,11 @@ def _load():
     lib.oracle_post_reorder.restype = ctypes.c_int
     lib.oracle_post_reorder.argtypes = [P, P, P, I64, I32, I32, P]
     lib.oracle_dense_layer.restype = ctypes.c_int
+    lib.oracle_permute_map.restype = ctypes.c_int
+    lib.oracle_permute_map.argtypes = [P, I64, I32, I32, I32, I32, I32, I64, P, P, P]
+    lib.oracle_dense_layer_map.restype = ctypes.c_int
+    lib.oracle_dense_layer_map.argtypes = [P, P, P, I64, I32, I32, I32, I32, I32, I32, I32, I32,
+                                           P, P, P, P, I32, P]
     lib.oracle_dense_layer.argtypes = [P, P, P, I64, I32, I32, I32, I32, I32, I32,
                                        P, P, P, P, I32, P]
     lib.oracle_set_threads.restype = None
@@ -135,8 +140,19 @@ def silu_mul_bf16(g: float, u: float) -> int:
 # ---- stages ---------------------------------------------------------------
 
 def select_experts(logits, bias, topk, n_group=1, topk_group=1, score_fn=0, renormalize=1,
-                   rsf=1.0, apply_rsf=1):
-    """Stage 1: returns (ids int32 [T, topk], weights fp32 [T, topk])."""
+                   rsf=1.0, apply_rsf=1, n_shared=0, shared_weight=1.0):
+    """Stage 1: returns (ids int32 [T, topk + n_shared], weights fp32 [T, topk + n_shared]).
+
+    Shared experts (this build's reading of the pages' shared-expert fusion):
+    every token also takes experts E..E+n_shared-1 with weight shared_weight,
+    after its routed slots."""
+    if n_shared:
+        ids, w = select_experts(logits, bias, topk, n_group, topk_group, score_fn, renormalize,
+                                rsf, apply_rsf)
+        T, E = np.asarray(logits).shape
+        sid = np.broadcast_to(np.arange(E, E + n_shared, dtype=np.int32), (T, n_shared))
+        sw = np.full((T, n_shared), shared_weight, dtype=np.float32)
+        return np.ascontiguousarray(np.concatenate([ids, sid], 1)), np.ascontiguousarray(np.concatenate([w, sw], 1))
     logits = _c(logits, np.float32)
     bias = _c(bias, np.float32)
     T, E = logits.shape
@@ -149,15 +165,17 @@ def select_experts(logits, bias, topk, n_group=1, topk_group=1, score_fn=0, reno
     return ids, w
 
 
-def permute(ids, expert_start, num_local, m_cap):
-    """Stage 2 (indices): returns (src2dst [T*topk], dst2src [m_cap], seg_indptr [num_local+1])."""
+def permute(ids, expert_start, num_local, m_cap, shared_base=0, n_shared=0):
+    """Stage 2 (indices): returns (src2dst [T*topk], dst2src [m_cap],
+    seg_indptr [num_local+n_shared+1]). num_local counts the routed local experts;
+    ids in [shared_base, shared_base + n_shared) are local experts num_local.."""
     ids = _c(ids, np.int32)
     T, topk = ids.shape
     src2dst = np.empty(T * topk, dtype=np.int32)
     dst2src = np.empty(max(m_cap, 0), dtype=np.int32)
-    seg = np.empty(num_local + 1, dtype=np.int32)
-    rc = _load().oracle_permute(_p(ids), T, topk, expert_start, num_local, m_cap,
-                                _p(src2dst), _p(dst2src), _p(seg))
+    seg = np.empty(num_local + n_shared + 1, dtype=np.int32)
+    rc = _load().oracle_permute_map(_p(ids), T, topk, expert_start, num_local, shared_base, n_shared,
+                                    m_cap, _p(src2dst), _p(dst2src), _p(seg))
     _check(rc, "permute")
     return src2dst, dst2src, seg
 
@@ -255,7 +273,7 @@ def post_reorder(down_bits, src2dst, weights, T, topk):
 
 
 def dense_layer(x_bits, ids, weights, I, expert_start, num_local, act_quant,
-                w13, s13, w2, s2, w_quant):
+                w13, s13, w2, s2, w_quant, shared_base=0, n_shared=0):
     """Dense per-token layer (no permutation): returns out bf16 bits [T, H]."""
     x_bits = _c(x_bits, np.uint16)
     ids = _c(ids, np.int32)
@@ -263,10 +281,11 @@ def dense_layer(x_bits, ids, weights, I, expert_start, num_local, act_quant,
     T, H = x_bits.shape
     topk = ids.shape[1]
     out = np.empty((T, H), dtype=np.uint16)
-    rc = _load().oracle_dense_layer(_p(x_bits), _p(ids), _p(w), T, H, I, topk, expert_start,
-                                    num_local, act_quant, _p(_c(w13, np.uint8)),
-                                    _p(_c(s13, np.float32)), _p(_c(w2, np.uint8)),
-                                    _p(_c(s2, np.float32)), w_quant, _p(out))
+    rc = _load().oracle_dense_layer_map(_p(x_bits), _p(ids), _p(w), T, H, I, topk, expert_start,
+                                        num_local, shared_base, n_shared, act_quant,
+                                        _p(_c(w13, np.uint8)), _p(_c(s13, np.float32)),
+                                        _p(_c(w2, np.uint8)), _p(_c(s2, np.float32)), w_quant,
+                                        _p(out))
     _check(rc, "dense_layer")
     return out
 
@@ -275,13 +294,14 @@ def layer(inp, flags=0):
     """Whole permuted layer on a workloads.LayerInputs; returns a dict of every stage's outputs."""
     cfg = inp.cfg
     ids, w = select_experts(inp.logits, inp.bias, cfg.topk, cfg.n_group, cfg.topk_group,
-                            cfg.score_fn, cfg.renormalize, cfg.rsf, cfg.apply_rsf)
+                            cfg.score_fn, cfg.renormalize, cfg.rsf, cfg.apply_rsf,
+                            cfg.n_shared, cfg.shared_weight)
     m_cap = cfg.m_cap
-    src2dst, dst2src, seg = permute(ids, cfg.expert_start, cfg.num_local, m_cap)
-    a13, s_a13 = pre_reorder_quant(inp.x, src2dst, cfg.topk, cfg.act_quant, m_cap)
+    src2dst, dst2src, seg = permute(ids, cfg.expert_start, cfg.num_local, m_cap, cfg.E, cfg.n_shared)
+    a13, s_a13 = pre_reorder_quant(inp.x, src2dst, cfg.slots, cfg.act_quant, m_cap)
     c13 = grouped_gemm(a13, s_a13, cfg.act_quant, inp.w13, inp.w13_scale, cfg.w_quant, seg, flags)
     a2, s_a2 = act_requant(c13, seg, cfg.act_quant)
     c2 = grouped_gemm(a2, s_a2, cfg.act_quant, inp.w2, inp.w2_scale, cfg.w_quant, seg, flags)
-    out = post_reorder(c2, src2dst, w, cfg.T, cfg.topk)
+    out = post_reorder(c2, src2dst, w, cfg.T, cfg.slots)
     return dict(ids=ids, weights=w, src2dst=src2dst, dst2src=dst2src, seg_indptr=seg,
                 a13=a13, a13_scale=s_a13, c13=c13, a2=a2, a2_scale=s_a2, c2=c2, out=out)

@@ -283,19 +283,35 @@ int oracle_select_experts(const float* logits, const float* bias, int64_t T, int
 /* (2) pre_reorder: permutation and dynamic FP8 quantisation                  */
 /* ------------------------------------------------------------------------- */
 
+/* Local expert index of a global expert id for one GPU's share: routed experts
+ * [expert_start, expert_start + num_routed) are local 0.., shared experts (ids
+ * [shared_base, shared_base + n_shared), appended to every token's slots) are
+ * local num_routed.., any other id is not local (-1). Shared experts treated as
+ * always-selected extra local experts is this build's reading of the pages'
+ * "shared expert fusion" (sglang PR #8364 review summary). */
+static int local_index(int id, int expert_start, int num_routed, int shared_base, int n_shared) {
+    int r = id - expert_start;
+    if (r >= 0 && r < num_routed) return r;
+    int q = id - shared_base;
+    if (q >= 0 && q < n_shared) return num_routed + q;
+    return -1;
+}
+
 /* Pairs f = t*topk + slot whose expert is local (expert_start <= id <
  * expert_start + num_local) are laid out expert by expert; inside an expert in
  * increasing f. seg_indptr[e] is the first row of local expert e,
  * seg_indptr[num_local] = M. Non-local pairs get src2dst = -1; rows M..m_cap-1
  * of dst2src are -1. */
-int oracle_permute(const int32_t* ids, int64_t T, int topk, int expert_start, int num_local,
-                   int64_t m_cap, int32_t* src2dst, int32_t* dst2src, int32_t* seg_indptr) {
+int oracle_permute_map(const int32_t* ids, int64_t T, int topk, int expert_start, int num_routed,
+                       int shared_base, int n_shared, int64_t m_cap, int32_t* src2dst,
+                       int32_t* dst2src, int32_t* seg_indptr) {
+    int num_local = num_routed + n_shared;
     int64_t P = T * topk;
     int64_t* cnt = (int64_t*)calloc(num_local + 1, sizeof(int64_t));
     int64_t* fill = (int64_t*)calloc(num_local + 1, sizeof(int64_t));
     for (int64_t f = 0; f < P; ++f) {
-        int e = ids[f] - expert_start;
-        if (e >= 0 && e < num_local) cnt[e]++;
+        int e = local_index(ids[f], expert_start, num_routed, shared_base, n_shared);
+        if (e >= 0) cnt[e]++;
     }
     int64_t run = 0;
     for (int e = 0; e < num_local; ++e) { seg_indptr[e] = (int32_t)run; run += cnt[e]; }
@@ -303,8 +319,8 @@ int oracle_permute(const int32_t* ids, int64_t T, int topk, int expert_start, in
     if (run > m_cap) { free(cnt); free(fill); return -3; }
     for (int64_t r = 0; r < m_cap; ++r) dst2src[r] = -1;
     for (int64_t f = 0; f < P; ++f) {
-        int e = ids[f] - expert_start;
-        if (e >= 0 && e < num_local) {
+        int e = local_index(ids[f], expert_start, num_routed, shared_base, n_shared);
+        if (e >= 0) {
             int64_t r = seg_indptr[e] + fill[e]++;
             src2dst[f] = (int32_t)r;
             dst2src[r] = (int32_t)f;
@@ -315,6 +331,12 @@ int oracle_permute(const int32_t* ids, int64_t T, int topk, int expert_start, in
     free(cnt);
     free(fill);
     return 0;
+}
+
+int oracle_permute(const int32_t* ids, int64_t T, int topk, int expert_start, int num_local,
+                   int64_t m_cap, int32_t* src2dst, int32_t* dst2src, int32_t* seg_indptr) {
+    return oracle_permute_map(ids, T, topk, expert_start, num_local, 0, 0, m_cap, src2dst, dst2src,
+                              seg_indptr);
 }
 
 /* Quantise token rows of x (bf16 [T,H]) into the expert-sorted rows named by
@@ -608,10 +630,10 @@ int oracle_router_logits(const uint16_t* x, const uint16_t* wg, int64_t T, int H
 /* For every token and every slot whose expert is local, run quantise -> w13 ->
  * SiLU-and-mul -> requantise -> w2 on the token's own row, then combine. Used
  * to check the permuted path (segments, src2dst, row-indexed scales). */
-int oracle_dense_layer(const uint16_t* x, const int32_t* ids, const float* w, int64_t T, int H,
-                       int I, int topk, int expert_start, int num_local, int act_quant,
-                       const uint8_t* w13, const float* s13, const uint8_t* w2, const float* s2,
-                       int w_quant, uint16_t* out) {
+int oracle_dense_layer_map(const uint16_t* x, const int32_t* ids, const float* w, int64_t T, int H,
+                           int I, int topk, int expert_start, int num_routed, int shared_base,
+                           int n_shared, int act_quant, const uint8_t* w13, const float* s13,
+                           const uint8_t* w2, const float* s2, int w_quant, uint16_t* out) {
     int N1 = 2 * I;
     int G1 = (H + QB - 1) / QB, G2 = (I + QB - 1) / QB;
     int64_t P = T * topk;
@@ -640,8 +662,8 @@ int oracle_dense_layer(const uint16_t* x, const int32_t* ids, const float* w, in
     float* bhat1 = (float*)malloc(sizeof(float) * (size_t)N1 * H);
     float* bhat2 = (float*)malloc(sizeof(float) * (size_t)H * I);
     for (int64_t f = 0; f < P; ++f) {
-        int e = ids[f] - expert_start;
-        if (e < 0 || e >= num_local) continue;
+        int e = local_index(ids[f], expert_start, num_routed, shared_base, n_shared);
+        if (e < 0) continue;
         int64_t t = f / topk;
         float sa_row[1024];
         for (int g = 0; g < G1; ++g) sa_row[g] = xs[t * G1 + g];
@@ -656,8 +678,8 @@ int oracle_dense_layer(const uint16_t* x, const int32_t* ids, const float* w, in
     if (act_quant == ACT_PER_TENSOR) {
         float amax = 0.0f;
         for (int64_t f = 0; f < P; ++f) {
-            int e = ids[f] - expert_start;
-            if (e < 0 || e >= num_local) continue;
+            int e = local_index(ids[f], expert_start, num_routed, shared_base, n_shared);
+            if (e < 0) continue;
             for (int i = 0; i < I; ++i) {
                 float a = fabsf(oracle_bf16_to_f32(h[f * I + i]));
                 if (a > amax) amax = a;
@@ -668,8 +690,8 @@ int oracle_dense_layer(const uint16_t* x, const int32_t* ids, const float* w, in
     uint8_t* hq = (uint8_t*)malloc(I);
     uint16_t* c2 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)P * H);
     for (int64_t f = 0; f < P; ++f) {
-        int e = ids[f] - expert_start;
-        if (e < 0 || e >= num_local) continue;
+        int e = local_index(ids[f], expert_start, num_routed, shared_base, n_shared);
+        if (e < 0) continue;
         float scales[1024];
         quant_row_bf16(h + f * I, I, act_quant, h_scale, h_inv, hq, scales);
         for (int k = 0; k < I; ++k) {
@@ -685,8 +707,7 @@ int oracle_dense_layer(const uint16_t* x, const int32_t* ids, const float* w, in
             double acc = 0.0;
             for (int j = 0; j < topk; ++j) {
                 int64_t f = t * topk + j;
-                int e = ids[f] - expert_start;
-                if (e < 0 || e >= num_local) continue;
+                if (local_index(ids[f], expert_start, num_routed, shared_base, n_shared) < 0) continue;
                 acc += (double)w[f] * (double)oracle_bf16_to_f32(c2[f * H + hh]);
             }
             out[t * H + hh] = oracle_bf16_rne_f64(acc);
@@ -694,6 +715,14 @@ int oracle_dense_layer(const uint16_t* x, const int32_t* ids, const float* w, in
     (void)G2;
     free(xq); free(xs); free(h); free(c13); free(ahat); free(bhat1); free(bhat2); free(hq); free(c2);
     return 0;
+}
+
+int oracle_dense_layer(const uint16_t* x, const int32_t* ids, const float* w, int64_t T, int H,
+                       int I, int topk, int expert_start, int num_local, int act_quant,
+                       const uint8_t* w13, const float* s13, const uint8_t* w2, const float* s2,
+                       int w_quant, uint16_t* out) {
+    return oracle_dense_layer_map(x, ids, w, T, H, I, topk, expert_start, num_local, 0, 0, act_quant,
+                                  w13, s13, w2, s2, w_quant, out);
 }
 
 /* ------------------------------------------------------------------------- */

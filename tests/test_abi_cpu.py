@@ -166,3 +166,19 @@ def test_router_select_rejects(lib):
     assert call(ng=3, sf=1) == moe.MOE_ERR_INVALID_ARG
     assert call(ids=None) == moe.MOE_ERR_NULL
     assert call(T=0) == moe.MOE_OK
+
+
+def test_shared_entry_points_reject(lib):
+    sel = lib.moe_select_experts_shared
+    def s(ns=1, k=2, E=8):
+        return sel(FAKE, None, 4, E, k, 1, 1, 0, 1, 1.0, 1, ns, 1.0, FAKE, FAKE, None)
+    assert s(ns=-1) == moe.MOE_ERR_INVALID_ARG
+    assert s(ns=63, k=2) == moe.MOE_ERR_UNSUPPORTED        # topk + n_shared > 64
+    pre = lib.moe_pre_reorder_quant_shared
+    def p(start=0, nr=8, base=8, ns=1, m_cap=36, nsc=36):
+        return pre(FAKE, FAKE, 4, 128, 9, start, nr, base, ns, 1, m_cap, FAKE, FAKE, nsc, FAKE, FAKE,
+                   FAKE, FAKE, 1 << 20, None)
+    assert p(base=4) == moe.MOE_ERR_INVALID_ARG             # shared ids inside the routed range
+    assert p(ns=65) == moe.MOE_ERR_INVALID_ARG
+    assert p(ns=-1) == moe.MOE_ERR_INVALID_ARG
+    assert p(m_cap=35, nsc=35) == moe.MOE_ERR_SHAPE         # m_cap < T * min(9, 9)

@@ -63,12 +63,24 @@ class MoEConfig:
     w_quant: int = W_PER_EXPERT
     zipf_skew: float = 0.0  # > 0: router logits biased so expert popularity follows Zipf(s)
     cold_experts: int = 0   # experts never drawn by the skew
+    n_shared: int = 0       # shared experts: ids E.., taken by every token, local after the routed
+    shared_weight: float = 1.0
     description: str = ""
 
     @property
+    def slots(self) -> int:
+        """Slots per token: the top-k routed ones plus the shared experts."""
+        return self.topk + self.n_shared
+
+    @property
+    def local_experts(self) -> int:
+        """Experts whose weights this GPU holds: routed local + shared."""
+        return self.num_local + self.n_shared
+
+    @property
     def m_cap(self) -> int:
-        """Upper bound on local (token, slot) pairs: T * min(topk, num_local)."""
-        return self.T * min(self.topk, self.num_local)
+        """Upper bound on local (token, slot) pairs: T * min(slots, local experts)."""
+        return self.T * min(self.slots, self.local_experts)
 
     def with_tokens(self, T: int) -> "MoEConfig":
         return dataclasses.replace(self, T=T)
@@ -101,6 +113,16 @@ CONFIGS = {
         description="128 experts all local, Zipf(1.2) popularity with 4 cold experts, "
                     "T=16384, 128x128 weight blocks and 1x128 activation groups"),
 }
+
+# Extension workloads (not in CONFIG_ORDER): the DeepSeek-V3 shares with the one
+# shared expert (intermediate 2048, weight 1 next to the rsf-scaled routed ones)
+# fused into the same grouped GEMMs.
+CONFIGS["dsv3_decode_ep_shared"] = dataclasses.replace(
+    CONFIGS["dsv3_decode_ep"], name="dsv3_decode_ep_shared", n_shared=1, shared_weight=1.0,
+    description="dsv3_decode_ep plus one shared expert (weight 1) fused as local expert 32")
+CONFIGS["dsv3_prefill_ep_shared"] = dataclasses.replace(
+    CONFIGS["dsv3_prefill_ep"], name="dsv3_prefill_ep_shared", n_shared=1, shared_weight=1.0,
+    description="dsv3_prefill_ep plus one shared expert (weight 1) fused as local expert 32")
 
 CONFIG_ORDER = ["tiny", "dsv3_decode_ep", "dsv3_prefill_ep", "mixtral", "skewed_block"]
 
@@ -241,7 +263,7 @@ def gen_weights(cfg: MoEConfig, which: str, seed: int = 0):
     import concurrent.futures as cf
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:
-        parts = list(ex.map(lambda e: gen_expert_weight(cfg, which, e, seed), range(cfg.num_local)))
+        parts = list(ex.map(lambda e: gen_expert_weight(cfg, which, e, seed), range(cfg.local_experts)))
     return np.stack([c for c, _ in parts]), np.stack([s.reshape(-1) for _, s in parts])
 
 
