@@ -59,6 +59,14 @@ def _load():
     lib.oracle_grouped_gemm.argtypes = [P, P, I32, P, P, I32, P, I32, I32, I32, P, I32]
     lib.oracle_grouped_gemm_rows.restype = ctypes.c_int
     lib.oracle_grouped_gemm_rows.argtypes = [P, P, I32, P, P, I32, P, I32, I32, I32, P, I64, P]
+    lib.oracle_e2m1_value.restype = ctypes.c_double
+    lib.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_value.restype = ctypes.c_double
+    lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_grouped_gemm_mxfp4.restype = ctypes.c_int
+    lib.oracle_grouped_gemm_mxfp4.argtypes = [P, P, I32, P, P, P, I32, P, I32, I32, I32, P]
+    lib.oracle_grouped_gemm_mxfp4_rows.restype = ctypes.c_int
+    lib.oracle_grouped_gemm_mxfp4_rows.argtypes = [P, P, I32, P, P, P, I32, P, I32, I32, I32, P, I64, P]
     lib.oracle_act_requant.restype = ctypes.c_int
     lib.oracle_act_requant.argtypes = [P, P, I32, I32, I32, P, P]
     lib.oracle_router_logits.restype = ctypes.c_int
@@ -231,6 +239,53 @@ def grouped_gemm_rows(a_q, a_scale, act_quant, b_q, b_scale, w_quant, seg_indptr
     return c
 
 
+def e2m1_value(nibble: int) -> float:
+    return float(_load().oracle_e2m1_value(int(nibble)))
+
+
+def e8m0_value(code: int) -> float:
+    return float(_load().oracle_e8m0_value(int(code)))
+
+
+def _fp4_args(a_q, b_fp4, b_e8m0):
+    a_q = _c(a_q, np.uint8)
+    b_fp4 = _c(b_fp4, np.uint8)
+    b_e8m0 = _c(b_e8m0, np.uint8)
+    K = a_q.shape[1]
+    num_local, N, Kh = b_fp4.shape
+    assert 2 * Kh == K and b_e8m0.shape == (num_local, N, K // 32)
+    return a_q, b_fp4, b_e8m0, num_local, N, K
+
+
+def grouped_gemm_mxfp4(a_q, a_scale, act_quant, b_fp4, b_e8m0, b_scale, w_quant, seg_indptr):
+    """Stage 3 with MXFP4 weights (packed codes [E_l, N, K/2], E8M0 [E_l, N, K/32]):
+    returns C bf16 bits [m_cap, N] (rows >= M are 0)."""
+    a_q, b_fp4, b_e8m0, num_local, N, K = _fp4_args(a_q, b_fp4, b_e8m0)
+    a_scale = _c(a_scale, np.float32)
+    b_scale = _c(b_scale, np.float32)
+    seg = _c(seg_indptr, np.int32)
+    c = np.zeros((a_q.shape[0], N), dtype=np.uint16)
+    rc = _load().oracle_grouped_gemm_mxfp4(_p(a_q), _p(a_scale), act_quant, _p(b_fp4), _p(b_e8m0),
+                                           _p(b_scale), w_quant, _p(seg), num_local, N, K, _p(c))
+    _check(rc, "grouped_gemm_mxfp4")
+    return c
+
+
+def grouped_gemm_mxfp4_rows(a_q, a_scale, act_quant, b_fp4, b_e8m0, b_scale, w_quant, seg_indptr, rows):
+    """grouped_gemm_mxfp4 for selected rows only: returns bf16 bits [len(rows), N]."""
+    a_q, b_fp4, b_e8m0, num_local, N, K = _fp4_args(a_q, b_fp4, b_e8m0)
+    a_scale = _c(a_scale, np.float32)
+    b_scale = _c(b_scale, np.float32)
+    seg = _c(seg_indptr, np.int32)
+    rows = _c(rows, np.int64)
+    c = np.zeros((len(rows), N), dtype=np.uint16)
+    rc = _load().oracle_grouped_gemm_mxfp4_rows(_p(a_q), _p(a_scale), act_quant, _p(b_fp4), _p(b_e8m0),
+                                                _p(b_scale), w_quant, _p(seg), num_local, N, K,
+                                                _p(rows), len(rows), _p(c))
+    _check(rc, "grouped_gemm_mxfp4_rows")
+    return c
+
+
 def act_requant(gateup_bits, seg_indptr, act_quant):
     """Stage 4: returns (a_q uint8 [m_cap, I], a_scale fp32)."""
     gu = _c(gateup_bits, np.uint16)
@@ -299,9 +354,17 @@ def layer(inp, flags=0):
     m_cap = cfg.m_cap
     src2dst, dst2src, seg = permute(ids, cfg.expert_start, cfg.num_local, m_cap, cfg.E, cfg.n_shared)
     a13, s_a13 = pre_reorder_quant(inp.x, src2dst, cfg.slots, cfg.act_quant, m_cap)
-    c13 = grouped_gemm(a13, s_a13, cfg.act_quant, inp.w13, inp.w13_scale, cfg.w_quant, seg, flags)
+    if cfg.w_fp4:
+        c13 = grouped_gemm_mxfp4(a13, s_a13, cfg.act_quant, inp.w13, inp.w13_e8m0, inp.w13_scale,
+                                 cfg.w_quant, seg)
+    else:
+        c13 = grouped_gemm(a13, s_a13, cfg.act_quant, inp.w13, inp.w13_scale, cfg.w_quant, seg, flags)
     a2, s_a2 = act_requant(c13, seg, cfg.act_quant)
-    c2 = grouped_gemm(a2, s_a2, cfg.act_quant, inp.w2, inp.w2_scale, cfg.w_quant, seg, flags)
+    if cfg.w_fp4:
+        c2 = grouped_gemm_mxfp4(a2, s_a2, cfg.act_quant, inp.w2, inp.w2_e8m0, inp.w2_scale,
+                                cfg.w_quant, seg)
+    else:
+        c2 = grouped_gemm(a2, s_a2, cfg.act_quant, inp.w2, inp.w2_scale, cfg.w_quant, seg, flags)
     out = post_reorder(c2, src2dst, w, cfg.T, cfg.slots)
     return dict(ids=ids, weights=w, src2dst=src2dst, dst2src=dst2src, seg_indptr=seg,
                 a13=a13, a13_scale=s_a13, c13=c13, a2=a2, a2_scale=s_a2, c2=c2, out=out)

@@ -22,6 +22,11 @@
  *   - top-k weighted combine: PR #8364 Motivation (moe_sum_reduce is the
  *     final weighted sum over the selected experts).
  *   - router projection (logits the gate scores): PR #8364 Motivation.
+ *   - FP4 expert weights: PR #8364 Summary of Changes, Highlights (the fusion
+ *     targets FP4-quantised MoE experts) and its benchmark commands (an FP4
+ *     checkpoint). The pages do not define the FP4 encoding; it is read as OCP
+ *     MXFP4 (E2M1 elements, one E8M0 scale per 32 elements along K), the
+ *     format the gfx950 matrix cores take natively.
  *
  * Precision: the GEMM accumulates in fp32 over dequantised FP8 operands. Every
  * step whose floating-point result decides an integer (expert ids, FP8 codes)
@@ -496,6 +501,96 @@ int oracle_grouped_gemm_rows(const uint8_t* a_q, const float* a_scale, int act_q
             for (int k = 0; k < K; ++k)
                 bhat[k] = oracle_e4m3_decode(b_q[((int64_t)e * N + n) * K + k])
                           * b_scale_at(b_scale, w_quant, e, n, k / QB, N, KB);
+            gemm_row(ahat, bhat, 1, K, out + n);
+        }
+        free(ahat);
+        free(bhat);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* (3b) grouped GEMM with MXFP4 weights                                        */
+/* ------------------------------------------------------------------------- */
+
+/* OCP Microscaling (MX) FP4 element, E2M1: bit 3 sign, bits 2..1 exponent
+ * (bias 1), bit 0 mantissa. Exponent field 0 is subnormal: 0.5 * m. Otherwise
+ * 2^(e-1) * (1 + m/2). No NaN or infinity; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double oracle_e2m1_value(uint8_t nibble) {
+    int s = (nibble >> 3) & 1, e = (nibble >> 1) & 3, m = nibble & 1;
+    double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* OCP MX shared scale, E8M0: 2^(s - 127); s = 255 is NaN. */
+double oracle_e8m0_value(uint8_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
+
+/* Element k of row n of expert e of packed MXFP4 weights [E, N, K/2]: byte
+ * k/2, the low nibble for even k, the high nibble for odd k. */
+static uint8_t fp4_code(const uint8_t* b_fp4, int e, int N, int K, int n, int k) {
+    uint8_t byte = b_fp4[((int64_t)e * N + n) * (K / 2) + k / 2];
+    return (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+}
+
+/* Bhat[n][k] = fp32( fp32(e2m1(code) * 2^(s[n][k/32]-127)) * sb(e, n) ): the
+ * block product is exact, the per-expert / per-channel factor rounds once. */
+static float fp4_bhat(const uint8_t* b_fp4, const uint8_t* b_e8m0, const float* b_scale, int w_quant,
+                      int e, int N, int K, int n, int k) {
+    float v = (float)(oracle_e2m1_value(fp4_code(b_fp4, e, N, K, n, k))
+                      * oracle_e8m0_value(b_e8m0[((int64_t)e * N + n) * (K / 32) + k / 32]));
+    float sb = w_quant == W_PER_EXPERT ? b_scale[e] : b_scale[(int64_t)e * N + n];
+    return v * sb;
+}
+
+/* Stage 3 with FP4 weights: for each local expert e and row r of its segment,
+ * C[r, n] = bf16( sum_k Ahat[r][k] * Bhat[e][n][k] ), fp32, k ascending, with
+ * Ahat as in the FP8 GEMM (activation scale at row r) and Bhat decoded from
+ * MXFP4 codes with one E8M0 scale per 32 consecutive K elements of a row.
+ * Weight factor modes: per expert or per output channel. K % 32 == 0. */
+int oracle_grouped_gemm_mxfp4(const uint8_t* a_q, const float* a_scale, int act_quant,
+                              const uint8_t* b_fp4, const uint8_t* b_e8m0, const float* b_scale,
+                              int w_quant, const int32_t* seg_indptr, int num_local, int N, int K,
+                              uint16_t* c) {
+    if (K % 32 != 0 || (w_quant != W_PER_EXPERT && w_quant != W_PER_CHANNEL)) return 1;
+    float* bhat = (float*)malloc(sizeof(float) * (size_t)N * K);
+    for (int e = 0; e < num_local; ++e) {
+        int64_t r0 = seg_indptr[e], r1 = seg_indptr[e + 1];
+        if (r1 <= r0) continue;
+#pragma omp parallel for schedule(static)
+        for (int n = 0; n < N; ++n)
+            for (int k = 0; k < K; ++k)
+                bhat[(int64_t)n * K + k] = fp4_bhat(b_fp4, b_e8m0, b_scale, w_quant, e, N, K, n, k);
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = r0; r < r1; ++r) {
+            float* ahat = (float*)malloc(sizeof(float) * K);
+            dequant_a_row(a_q, a_scale, act_quant, r, r, K, ahat);
+            gemm_row(ahat, bhat, N, K, c + r * N);
+            free(ahat);
+        }
+    }
+    free(bhat);
+    return 0;
+}
+
+/* Selected output rows of oracle_grouped_gemm_mxfp4 (zeros outside every segment). */
+int oracle_grouped_gemm_mxfp4_rows(const uint8_t* a_q, const float* a_scale, int act_quant,
+                                   const uint8_t* b_fp4, const uint8_t* b_e8m0, const float* b_scale,
+                                   int w_quant, const int32_t* seg_indptr, int num_local, int N,
+                                   int K, const int64_t* rows, int64_t nrows, uint16_t* c_rows) {
+    if (K % 32 != 0 || (w_quant != W_PER_EXPERT && w_quant != W_PER_CHANNEL)) return 1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t r = rows[i];
+        int e = -1;
+        for (int q = 0; q < num_local; ++q)
+            if (r >= seg_indptr[q] && r < seg_indptr[q + 1]) e = q;
+        uint16_t* out = c_rows + i * N;
+        if (e < 0) { memset(out, 0, sizeof(uint16_t) * (size_t)N); continue; }
+        float* ahat = (float*)malloc(sizeof(float) * K);
+        float* bhat = (float*)malloc(sizeof(float) * (size_t)K);
+        dequant_a_row(a_q, a_scale, act_quant, r, r, K, ahat);
+        for (int n = 0; n < N; ++n) {
+            for (int k = 0; k < K; ++k) bhat[k] = fp4_bhat(b_fp4, b_e8m0, b_scale, w_quant, e, N, K, n, k);
             gemm_row(ahat, bhat, 1, K, out + n);
         }
         free(ahat);

@@ -65,6 +65,7 @@ class MoEConfig:
     cold_experts: int = 0   # experts never drawn by the skew
     n_shared: int = 0       # shared experts: ids E.., taken by every token, local after the routed
     shared_weight: float = 1.0
+    w_fp4: bool = False     # expert weights as MXFP4 codes + E8M0 block scales (w_quant: the fp32 factor)
     description: str = ""
 
     @property
@@ -123,6 +124,16 @@ CONFIGS["dsv3_decode_ep_shared"] = dataclasses.replace(
 CONFIGS["dsv3_prefill_ep_shared"] = dataclasses.replace(
     CONFIGS["dsv3_prefill_ep"], name="dsv3_prefill_ep_shared", n_shared=1, shared_weight=1.0,
     description="dsv3_prefill_ep plus one shared expert (weight 1) fused as local expert 32")
+
+# FP4-weight extension workloads: the same DeepSeek-V3 shares with MXFP4 expert
+# weights (E2M1 codes, one E8M0 scale per 32 input elements, and a per-expert
+# fp32 factor).
+CONFIGS["dsv3_decode_ep_fp4"] = dataclasses.replace(
+    CONFIGS["dsv3_decode_ep"], name="dsv3_decode_ep_fp4", w_fp4=True, w_quant=W_PER_EXPERT,
+    description="dsv3_decode_ep with MXFP4 expert weights")
+CONFIGS["dsv3_prefill_ep_fp4"] = dataclasses.replace(
+    CONFIGS["dsv3_prefill_ep"], name="dsv3_prefill_ep_fp4", w_fp4=True, w_quant=W_PER_EXPERT,
+    description="dsv3_prefill_ep with MXFP4 expert weights")
 
 CONFIG_ORDER = ["tiny", "dsv3_decode_ep", "dsv3_prefill_ep", "mixtral", "skewed_block"]
 
@@ -255,6 +266,44 @@ def gen_expert_weight(cfg: MoEConfig, which: str, e_local: int, seed: int = 0):
     return codes, s
 
 
+# Magnitude ranks 0..7 of E2M1 codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6) are drawn
+# with these probabilities (a bell shape, like block-quantised Gaussian weights).
+FP4_RANK_P = np.array([0.20, 0.22, 0.20, 0.14, 0.10, 0.08, 0.04, 0.02])
+FP4_E8M0_BASE = 120  # block scales 2^(119..121 - 127)
+
+
+def gen_expert_weight_fp4(cfg: MoEConfig, which: str, e_local: int, seed: int = 0):
+    """One local expert's MXFP4 weight: packed codes uint8 [N, K/2] (element k in
+    byte k/2, low nibble for even k), E8M0 block scales uint8 [N, K/32], and the
+    fp32 per-expert factor [1] (or per channel [N] under W_PER_CHANNEL).
+    Codes and scales are drawn directly: nothing is quantised here."""
+    if which == "w13":
+        N, K, tid = 2 * cfg.I, cfg.H, TID_W13
+    elif which == "w2":
+        N, K, tid = cfg.H, cfg.I, TID_W2
+    else:
+        raise ValueError(which)
+    g = rng(seed, tid, cfg.expert_start + e_local, 4)
+    rank = g.choice(8, size=(N, K), p=FP4_RANK_P).astype(np.uint8)
+    sign = g.integers(0, 2, size=(N, K), dtype=np.uint8)
+    nib = rank | (sign << 3)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    e8m0 = (FP4_E8M0_BASE + g.integers(-1, 2, size=(N, K // 32))).astype(np.uint8)
+    n_f = 1 if cfg.w_quant == W_PER_EXPERT else N
+    factor = g.uniform(0.75, 1.25, size=n_f).astype(np.float32)
+    return packed, e8m0, factor
+
+
+def gen_weights_fp4(cfg: MoEConfig, which: str, seed: int = 0):
+    """All local experts: packed [E_l, N, K/2], e8m0 [E_l, N, K/32], factors [E_l, 1 or N]."""
+    import concurrent.futures as cf
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        parts = list(ex.map(lambda e: gen_expert_weight_fp4(cfg, which, e, seed), range(cfg.local_experts)))
+    return (np.stack([p for p, _, _ in parts]), np.stack([s for _, s, _ in parts]),
+            np.stack([f for _, _, f in parts]))
+
+
 def gen_weights(cfg: MoEConfig, which: str, seed: int = 0):
     """All local experts' codes [E_l, N, K] uint8 and scales fp32 (mode-shaped, flattened per expert).
 
@@ -277,18 +326,24 @@ class LayerInputs:
     w13_scale: np.ndarray   # fp32 [E_l, ...]
     w2: np.ndarray          # uint8 [E_l, H, I]
     w2_scale: np.ndarray
+    w13_e8m0: Optional[np.ndarray] = None  # MXFP4 weights only: w13 / w2 are then packed
+    w2_e8m0: Optional[np.ndarray] = None   # [E_l, N, K/2] and these the [E_l, N, K/32] scales
 
 
 def gen_layer_inputs(cfg: MoEConfig, seed: int = 0, weights: bool = True) -> LayerInputs:
     x = gen_tokens(cfg, seed)
     logits = gen_logits(cfg, x, seed)
     bias = gen_bias(cfg, seed)
-    if weights:
+    e13 = e2 = None
+    if weights and cfg.w_fp4:
+        w13, e13, s13 = gen_weights_fp4(cfg, "w13", seed)
+        w2, e2, s2 = gen_weights_fp4(cfg, "w2", seed)
+    elif weights:
         w13, s13 = gen_weights(cfg, "w13", seed)
         w2, s2 = gen_weights(cfg, "w2", seed)
     else:
         w13 = s13 = w2 = s2 = None
-    return LayerInputs(cfg, x, logits, bias, w13, s13, w2, s2)
+    return LayerInputs(cfg, x, logits, bias, w13, s13, w2, s2, e13, e2)
 
 
 def a_scale_numel(mode: int, m_cap: int, K: int) -> int:
