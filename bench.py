@@ -48,14 +48,17 @@ def parse():
 
 
 def algorithmic_work(cfg, seg, a_scale_bytes13, a_scale_bytes2, w13_scale_numel, w2_scale_numel):
-    """Bytes each stage must move (inputs read once, outputs written once) and GEMM FLOPs."""
+    """Bytes each stage must move (inputs read once, outputs written once) and GEMM FLOPs.
+    Weights of experts with rows: e4m3 codes (1 byte each) or MXFP4 (half a byte
+    each plus one E8M0 byte per 32), and their fp32 scales."""
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.slots
     M = int(seg[-1])
     counts = np.diff(seg)
     nonempty = int((counts > 0).sum())
     El = cfg.local_experts
-    b13 = nonempty * 2 * I * H + w13_scale_numel * 4 * nonempty // max(El, 1)
-    b2 = nonempty * H * I + w2_scale_numel * 4 * nonempty // max(El, 1)
+    per_w = (0.5 + 1.0 / 32) if cfg.w_fp4 else 1.0
+    b13 = int(nonempty * 2 * I * H * per_w) + w13_scale_numel * 4 * nonempty // max(El, 1)
+    b2 = int(nonempty * H * I * per_w) + w2_scale_numel * 4 * nonempty // max(El, 1)
     tok_local = None
     work = {}
     work["select"] = dict(bytes=T * E * 4 + (E * 4 if cfg.use_bias else 0) + T * k * 8, flops=0)
@@ -74,23 +77,14 @@ def algorithmic_work(cfg, seg, a_scale_bytes13, a_scale_bytes2, w13_scale_numel,
     return work, M, nonempty
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
+STAGES = ["select", "pre_reorder", "gemm_w13", "act_requant", "gemm_w2", "post_reorder"]
 
-    import torch
-    import fp8_grouped_gemm_select_amd as moe
-    import workloads as W
 
-    cfg = W.CONFIGS[args.config]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    t0 = time.time()
-    inp = W.gen_layer_inputs(cfg, seed=args.seed)
-
+def time_layer(cfg, inp, steps, warmup, moe, torch, dev):
+    """Upload one workload's inputs, run `warmup` untimed layer passes, then time
+    exactly `steps` passes (wall clock between synchronisations) with HIP events
+    between the stages on the launch stream. Returns (ms per step, mean ms per
+    stage, the layer buffers, the two weight-scale tensors)."""
     def up(a, dtype=None):
         t = torch.from_numpy(np.ascontiguousarray(a))
         if dtype is not None:
@@ -102,17 +96,12 @@ def main():
     bias = up(inp.bias) if inp.bias is not None else None
     w13, s13 = up(inp.w13), up(inp.w13_scale.reshape(-1))
     w2, s2 = up(inp.w2), up(inp.w2_scale.reshape(-1))
+    e13 = up(inp.w13_e8m0) if cfg.w_fp4 else None
+    e2 = up(inp.w2_e8m0) if cfg.w_fp4 else None
     buf = moe.LayerBuffers.allocate(cfg.T, cfg.H, cfg.I, cfg.topk, cfg.num_local, cfg.act_quant,
                                     n_shared=cfg.n_shared)
-    gen_s = time.time() - t0
-    print(f"[bench] {cfg.name}: inputs ready in {gen_s:.1f}s", file=sys.stderr, flush=True)
 
-    kw = dict(topk=cfg.topk, n_group=cfg.n_group, topk_group=cfg.topk_group,
-              score_fn=cfg.score_fn, renormalize=cfg.renormalize,
-              routed_scaling_factor=cfg.rsf, apply_rsf=cfg.apply_rsf,
-              expert_start=cfg.expert_start, num_local=cfg.num_local, act_quant=cfg.act_quant,
-              w_quant=cfg.w_quant)
-    stages = ["select", "pre_reorder", "gemm_w13", "act_requant", "gemm_w2", "post_reorder"]
+    stages = STAGES
 
     def step(events=None):
         def mark(i):
@@ -144,34 +133,66 @@ def main():
                                       expert_start=cfg.expert_start, num_local=cfg.num_local,
                                       act_quant=cfg.act_quant)
         mark(2)
-        moe.moe_grouped_gemm_fp8(buf.a13, buf.a13_scale, w13, s13, buf.seg_indptr, buf.c13,
-                                 act_quant=cfg.act_quant, w_quant=cfg.w_quant)
+        if cfg.w_fp4:
+            moe.moe_grouped_gemm_mxfp4(buf.a13, buf.a13_scale, w13, e13, s13, buf.seg_indptr, buf.c13,
+                                       act_quant=cfg.act_quant, w_quant=cfg.w_quant)
+        else:
+            moe.moe_grouped_gemm_fp8(buf.a13, buf.a13_scale, w13, s13, buf.seg_indptr, buf.c13,
+                                     act_quant=cfg.act_quant, w_quant=cfg.w_quant)
         mark(3)
         moe.moe_act_requant(buf.c13, buf.seg_indptr, buf.a2, buf.a2_scale, buf.workspace,
                             act_quant=cfg.act_quant)
         mark(4)
-        moe.moe_grouped_gemm_fp8(buf.a2, buf.a2_scale, w2, s2, buf.seg_indptr, buf.c2,
-                                 act_quant=cfg.act_quant, w_quant=cfg.w_quant)
+        if cfg.w_fp4:
+            moe.moe_grouped_gemm_mxfp4(buf.a2, buf.a2_scale, w2, e2, s2, buf.seg_indptr, buf.c2,
+                                       act_quant=cfg.act_quant, w_quant=cfg.w_quant)
+        else:
+            moe.moe_grouped_gemm_fp8(buf.a2, buf.a2_scale, w2, s2, buf.seg_indptr, buf.c2,
+                                     act_quant=cfg.act_quant, w_quant=cfg.w_quant)
         mark(5)
         moe.moe_post_reorder(buf.c2, buf.src2dst, buf.topk_weights, buf.out)
         mark(6)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` layer passes; HIP events on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         step(ev[s])
     torch.cuda.synchronize()
     t_end = time.perf_counter()
-    ms_per_step = (t_end - t_start) * 1e3 / args.steps
-    stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+    ms_per_step = (t_end - t_start) * 1e3 / steps
+    stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
                 for i, name in enumerate(stages)}
 
+    return ms_per_step, stage_ms, buf, s13, s2
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import fp8_grouped_gemm_select_amd as moe
+    import workloads as W
+
+    cfg = W.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    inp = W.gen_layer_inputs(cfg, seed=args.seed)
+
+    gen_s = time.time() - t0
+    print(f"[bench] {cfg.name}: inputs ready in {gen_s:.1f}s", file=sys.stderr, flush=True)
+    ms_per_step, stage_ms, buf, s13, s2 = time_layer(cfg, inp, args.steps, args.warmup, moe, torch, dev)
+    stages = STAGES
     seg = buf.seg_indptr.cpu().numpy()
     work, M, nonempty = algorithmic_work(cfg, seg, buf.a13_scale.numel() * 4, buf.a2_scale.numel() * 4,
                                          s13.numel(), s2.numel())
@@ -210,17 +231,24 @@ def main():
     result = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp4e2m1" if cfg.w_fp4 else "fp8e4m3",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
                    "topk": cfg.topk, "num_local": cfg.num_local, "n_shared": cfg.n_shared, "M": M,
                    "experts_with_rows": nonempty, "act_quant": cfg.act_quant,
-                   "w_quant": cfg.w_quant, "parallelism": "single GPU (one EP share)"},
+                   "w_quant": cfg.w_quant, "w_format": "mxfp4" if cfg.w_fp4 else "e4m3",
+                   "parallelism": "single GPU (one EP share)"},
         "roofline": roof, "gemm": gemm, "stages": stage_stats,
     }
 
     if not args.no_next_rows:
         result["next_rows"] = {"router_select": time_router_select(cfg, inp, args, moe, W, torch, dev)}
+        fp4_name = cfg.name + "_fp4"
+        if not cfg.w_fp4 and fp4_name in W.CONFIGS:
+            del buf
+            torch.cuda.empty_cache()
+            result["next_rows"]["fp4_layer"] = time_fp4_layer(W.CONFIGS[fp4_name], args, moe, W, torch, dev)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20)
@@ -235,6 +263,28 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)
+
+
+def time_fp4_layer(cfg, args, moe, W, torch, dev):
+    """The same layer with MXFP4 expert weights, timed on its own (not in `value`)."""
+    inp = W.gen_layer_inputs(cfg, seed=args.seed)
+    ms, stage_ms, buf, s13, s2 = time_layer(cfg, inp, args.steps, args.warmup, moe, torch, dev)
+    seg = buf.seg_indptr.cpu().numpy()
+    work, M, _ = algorithmic_work(cfg, seg, buf.a13_scale.numel() * 4, buf.a2_scale.numel() * 4,
+                                  s13.numel(), s2.numel())
+    out = dict(workload=cfg.name, tokens_per_s=round(cfg.T / (ms * 1e-3), 1), ms_per_step=round(ms, 4),
+               note="MXFP4 expert weights (E2M1 + E8M0 per 32), same routing and activations; not in value")
+    for name in ("gemm_w13", "gemm_w2"):
+        t = stage_ms[name] * 1e-3
+        out[name] = dict(us=round(stage_ms[name] * 1e3, 2),
+                         GBps=round(work[name]["bytes"] / t / 1e9, 1),
+                         hbm_frac=round(work[name]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+                         TFLOPs=round(work[name]["flops"] / t / 1e12, 1),
+                         mfma_frac=round(work[name]["flops"] / t / 1e12 / FP8_PEAK_TFLOPS, 4),
+                         algorithmic_bytes=int(work[name]["bytes"]))
+    del buf
+    torch.cuda.empty_cache()
+    return out
 
 
 def time_router_select(cfg, inp, args, moe, W, torch, dev):

@@ -31,7 +31,8 @@ W_PER_EXPERT, W_PER_CHANNEL, W_BLOCK = 0, 1, 2
 
 EXPORTS = ["moe_select_experts", "moe_workspace_bytes", "moe_pre_reorder_quant",
            "moe_grouped_gemm_fp8", "moe_act_requant", "moe_post_reorder", "moe_status_string",
-           "moe_router_select", "moe_select_experts_shared", "moe_pre_reorder_quant_shared"]
+           "moe_router_select", "moe_select_experts_shared", "moe_pre_reorder_quant_shared",
+           "moe_grouped_gemm_mxfp4"]
 
 _lib = None
 
@@ -65,6 +66,9 @@ def load_library():
     lib.moe_grouped_gemm_fp8.restype = ctypes.c_int
     lib.moe_grouped_gemm_fp8.argtypes = [P, P, I64, I32, P, P, I64, I32, P, I32, I64, I32, I32,
                                          P, P]
+    lib.moe_grouped_gemm_mxfp4.restype = ctypes.c_int
+    lib.moe_grouped_gemm_mxfp4.argtypes = [P, P, I64, I32, P, P, P, I64, I32, P, I32, I64, I32, I32,
+                                           P, P]
     lib.moe_act_requant.restype = ctypes.c_int
     lib.moe_act_requant.argtypes = [P, P, I32, I64, I32, I32, P, P, I64, P, SZ, P]
     lib.moe_post_reorder.restype = ctypes.c_int
@@ -233,6 +237,24 @@ def moe_grouped_gemm_fp8(a_q, a_scale, b_q, b_scale, seg_indptr, c, *, act_quant
         b_scale.numel(), w_quant, _ptr(seg_indptr), num_local, m_cap, N, K, _ptr(c),
         _stream(stream))
     _check(rc, "moe_grouped_gemm_fp8")
+
+
+def moe_grouped_gemm_mxfp4(a_q, a_scale, b_fp4, b_e8m0, b_scale, seg_indptr, c, *, act_quant, w_quant,
+                           stream=None):
+    """Stage 3 with MXFP4 weights: b_fp4 uint8 [E_l, N, K/2] packed E2M1 codes,
+    b_e8m0 uint8 [E_l, N, K/32] block scales, b_scale fp32 factor."""
+    _dtype(a_q, torch.uint8, torch.float8_e4m3fn, name="a_q")
+    _dtype(b_fp4, torch.uint8, name="b_fp4")
+    _dtype(b_e8m0, torch.uint8, name="b_e8m0")
+    _dtype(c, torch.bfloat16, name="c")
+    m_cap, K = a_q.shape
+    num_local, N, Kh = b_fp4.shape
+    if 2 * Kh != K or tuple(b_e8m0.shape) != (num_local, N, K // 32):
+        raise ValueError("a_q, b_fp4 and b_e8m0 disagree on K")
+    rc = load_library().moe_grouped_gemm_mxfp4(
+        _ptr(a_q), _ptr(a_scale), a_scale.numel(), act_quant, _ptr(b_fp4), _ptr(b_e8m0), _ptr(b_scale),
+        b_scale.numel(), w_quant, _ptr(seg_indptr), num_local, m_cap, N, K, _ptr(c), _stream(stream))
+    _check(rc, "moe_grouped_gemm_mxfp4")
 
 
 def moe_act_requant(gateup, seg_indptr, a_q, a_scale, workspace, *, act_quant, stream=None):

@@ -70,6 +70,21 @@ __device__ __forceinline__ v8i lds_operand(const uint8_t* lds, int row, int lane
     return v;
 }
 
+// The e4m3 operand of the scaled MFMA with an E2M1 first operand: the hardware
+// pairs the e4m3 lane's low 16 bytes with K [16 (l/16), +16) and its high 16
+// bytes with K [64 + 16 (l/16), +16) of the E2M1 operand, whose lane l holds
+// the 32 elements of K block l/16 (measured on gfx950). So lane l reads chunks
+// l/16 and l/16 + 4 of the row.
+__device__ __forceinline__ v8i lds_operand_x4(const uint8_t* lds, int row, int lane) {
+    const int c = lane >> 4;
+    const uint4 lo = *(const uint4*)(lds + swz(row, c));
+    const uint4 hi = *(const uint4*)(lds + swz(row, c + 4));
+    v8i v;
+    v[0] = (int)lo.x; v[1] = (int)lo.y; v[2] = (int)lo.z; v[3] = (int)lo.w;
+    v[4] = (int)hi.x; v[5] = (int)hi.y; v[6] = (int)hi.z; v[7] = (int)hi.w;
+    return v;
+}
+
 // Epilogue staging: a wave's 64 x 64 bf16 block, rows of 128 bytes, 16-byte
 // chunk q of row r at q ^ (r & 7).
 __device__ __forceinline__ int ep_off(int r, int q) { return r * 128 + ((q ^ (r & 7)) << 4); }
@@ -301,6 +316,16 @@ constexpr int kDStage = (DBM + DBN) * DBK;      // 48 KB
 constexpr int kDmaA = DBM * DBK / 1024 / 8;     // 1 KB DMA instructions per wave per stage: 2
 constexpr int kDmaB = DBN * DBK / 1024 / 8;     // 4
 constexpr int kDma = kDmaA + kDmaB;             // 6
+// MXFP4 weights: a stage's B tile is 256 rows of 64 bytes (128 E2M1 codes)
+// followed by the rows' E8M0 scales of the step (one dword per row).
+constexpr int kDmaB4 = DBN * DBK / 2 / 1024 / 8;  // 2
+constexpr int kDStageS4 = kDStageA + DBN * DBK / 2;  // scale dwords at +32 KB
+constexpr int kDma4 = kDmaA + kDmaB4 + 1;         // 5 (A, B, scales)
+
+// Chunk position of 16-byte chunk c of a 64-byte B row r (FP4): c ^ ((r >> 2) & 3).
+// Sixteen consecutive rows read at one chunk hit sixteen distinct 16-byte bank
+// groups of the 64-bank LDS.
+__device__ __forceinline__ int fp4_pos(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 // One 16-byte global -> LDS DMA per lane: from base + voff (base wave-uniform
 // in SGPRs, voff a per-lane 32-bit offset) to LDS address lds_base + 16 * lane
@@ -308,6 +333,14 @@ constexpr int kDma = kDmaA + kDmaB;             // 6
 // no waits of its own around it; every wait on these loads is explicit.
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_base)
+                 : "memory");
+}
+
+// One 4-byte global -> LDS DMA per lane, to LDS address lds_base + 4 * lane.
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                  :
                  : "v"(voff), "s"(base), "s"(lds_base)
                  : "memory");
@@ -332,15 +365,22 @@ struct DTile {
     int e, row0, row_end, n0, a_rows, b_rows, sa_row, nb_w;
     const uint8_t* a_g;
     const uint8_t* b_g;
-    uint32_t a_off[kDmaA], b_off[kDmaB];
+    const uint8_t* s_g;  // FP4: E8M0 scales of the tile's first weight row
+    uint32_t a_off[kDmaA], b_off[kDmaB], s_off;
 };
 
-template <bool KDEP>
+// FP4: B holds MXFP4 weights (packed E2M1 [E, N, K/2], element k in byte k/2,
+// low nibble for even k) with E8M0 scales Be8 [E, N, K/32]; the MFMA takes the
+// codes as its first operand (format E2M1) with the row's scale byte of the
+// lane's 32-element block, the activations as e4m3 with scale 2^0.
+template <bool KDEP, bool FP4>
 __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sa, int act_quant,
-    const uint8_t* __restrict__ B, const float* __restrict__ sb, int w_quant,
-    const int32_t* __restrict__ seg_in, int num_local, int64_t m_cap, int N, int K,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Be8, const float* __restrict__ sb,
+    int w_quant, const int32_t* __restrict__ seg_in, int num_local, int64_t m_cap, int N, int K,
     uint16_t* __restrict__ C) {
+    static_assert(!(KDEP && FP4), "FP4 weights take no K-dependent scales");
+    constexpr int kDmaN = FP4 ? kDma4 : kDma;
     __shared__ __align__(16) uint8_t lds[kDStages * kDStage];
     __shared__ int s_seg[kMaxLocal + 1];
     __shared__ int s_tstart[kMaxLocal + 1];
@@ -385,27 +425,54 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
             const int g = r < t.a_rows ? r : t.a_rows - 1;
             t.a_off[i] = (uint32_t)g * (uint32_t)K + (uint32_t)((((lane & 7) ^ perm8(r)) << 4));
         }
+        if (FP4) {
+            // instruction i of wave w fills 64-byte rows 16 (2 w + i) + lane / 4 at
+            // position lane % 4; the scale DMA of wave w loads the dwords of rows
+            // 64 (w % 4) + lane (waves w and w + 4 write the same values)
 #pragma unroll
-        for (int i = 0; i < kDmaB; ++i) {
-            const int r = (wid * kDmaB + i) * 8 + (lane >> 3);
-            const int g = r < t.b_rows ? r : t.b_rows - 1;
-            t.b_off[i] = (uint32_t)g * (uint32_t)K + (uint32_t)((((lane & 7) ^ perm8(r)) << 4));
+            for (int i = 0; i < kDmaB4; ++i) {
+                const int r = (wid * kDmaB4 + i) * 16 + (lane >> 2);
+                const int g = r < t.b_rows ? r : t.b_rows - 1;
+                t.b_off[i] = (uint32_t)g * (uint32_t)(K / 2) + (uint32_t)(fp4_pos(r, lane & 3) << 4);
+            }
+            const int rs = (wid & 3) * 64 + lane;
+            t.s_off = (uint32_t)(rs < t.b_rows ? rs : t.b_rows - 1) * (uint32_t)(K / 32);
+            t.b_g = B + ((int64_t)t.e * N + t.n0) * (K / 2);
+            t.s_g = Be8 + ((int64_t)t.e * N + t.n0) * (K / 32);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kDmaB; ++i) {
+                const int r = (wid * kDmaB + i) * 8 + (lane >> 3);
+                const int g = r < t.b_rows ? r : t.b_rows - 1;
+                t.b_off[i] = (uint32_t)g * (uint32_t)K + (uint32_t)((((lane & 7) ^ perm8(r)) << 4));
+            }
+            t.b_g = B + ((int64_t)t.e * N + t.n0) * K;
+            t.s_g = nullptr;
+            t.s_off = 0;
         }
         t.a_g = A + (int64_t)t.row0 * K;
-        t.b_g = B + ((int64_t)t.e * N + t.n0) * K;
         t.sa_row = t.row0 + ((tid & (DBM - 1)) < t.a_rows ? (tid & (DBM - 1)) : t.a_rows - 1);
         return t;
     };
     auto issue = [&](const DTile& t, int k) {  // DMA of K step k into stage k % 3
         const uint32_t st = lds0 + (uint32_t)((k % kDStages) * kDStage);
         const uint8_t* ab = uniform_ptr(t.a_g + k * DBK);
-        const uint8_t* bb = uniform_ptr(t.b_g + k * DBK);
         const uint32_t la = __builtin_amdgcn_readfirstlane(st + wid * kDmaA * 1024);
-        const uint32_t lb = __builtin_amdgcn_readfirstlane(st + kDStageA + wid * kDmaB * 1024);
 #pragma unroll
         for (int i = 0; i < kDmaA; ++i) dma16(ab, t.a_off[i], la + i * 1024);
+        if (FP4) {
+            const uint8_t* bb = uniform_ptr(t.b_g + k * (DBK / 2));
+            const uint32_t lb = __builtin_amdgcn_readfirstlane(st + kDStageA + wid * kDmaB4 * 1024);
 #pragma unroll
-        for (int i = 0; i < kDmaB; ++i) dma16(bb, t.b_off[i], lb + i * 1024);
+            for (int i = 0; i < kDmaB4; ++i) dma16(bb, t.b_off[i], lb + i * 1024);
+            const uint8_t* sbp = uniform_ptr(t.s_g + k * (DBK / 32));
+            dma4(sbp, t.s_off, __builtin_amdgcn_readfirstlane(st + kDStageS4 + (wid & 3) * 256));
+        } else {
+            const uint8_t* bb = uniform_ptr(t.b_g + k * DBK);
+            const uint32_t lb = __builtin_amdgcn_readfirstlane(st + kDStageA + wid * kDmaB * 1024);
+#pragma unroll
+            for (int i = 0; i < kDmaB; ++i) dma16(bb, t.b_off[i], lb + i * 1024);
+        }
     };
 
     int lt = lt_begin + slot;
@@ -447,7 +514,7 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
             for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
         for (int k = 0; k < nk; ++k) {
-            if (k + 1 < nk) wait_vmcnt<kDma>();
+            if (k + 1 < nk) wait_vmcnt<kDmaN>();
             else wait_vmcnt<0>();
             if (group_act && tid < DBM) s_sa[k % kDStages][tid] = q;
             __syncthreads();  // stage k complete; every wave is done with stage k-1
@@ -457,29 +524,50 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
             const uint8_t* la = lds + (k % kDStages) * kDStage;
             const uint8_t* lb = la + kDStageA;
             v8i af[4], bfr[4];
+            if (FP4) {
+                // lane l: 16 bytes = the 32 codes of K block l / 16 of row l % 16,
+                // and that block's E8M0 scale; the activations in the matching order
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = lds_operand(la, wm * 64 + i * 16 + (lane & 15), lane);
+                for (int i = 0; i < 4; ++i) af[i] = lds_operand_x4(la, wm * 64 + i * 16 + (lane & 15), lane);
+                const uint8_t* lsc = la + kDStageS4;
+                int scl[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bfr[j] = lds_operand(lb, wn * 64 + j * 16 + (lane & 15), lane);
-
-            if (!KDEP) {
+                for (int j = 0; j < 4; ++j) {
+                    const int rb = wn * 64 + j * 16 + (lane & 15);
+                    const uint4 q = *(const uint4*)(lb + rb * 64 + (fp4_pos(rb, lane >> 4) << 4));
+                    bfr[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+                    scl[j] = (int)lsc[rb * 4 + (lane >> 4)];
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            bfr[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+                            bfr[j], af[i], acc[i][j], 4, 0, 0, scl[j], 0, 127);
             } else {
-                const float sbv = block_w ? sb[((int64_t)cur.e * NB + cur.nb_w) * KB + k] : 1.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float f = (group_act ? s_sa[k % kDStages][wm * 64 + i * 16 + (lane & 15)] : 1.0f) * sbv;
+                for (int i = 0; i < 4; ++i) af[i] = lds_operand(la, wm * 64 + i * 16 + (lane & 15), lane);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            bfr[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                for (int j = 0; j < 4; ++j) bfr[j] = lds_operand(lb, wn * 64 + j * 16 + (lane & 15), lane);
+                if (!KDEP) {
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) acc[i][j][v] = acc[i][j][v] + t[v] * f;
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                bfr[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+                } else {
+                    const float sbv = block_w ? sb[((int64_t)cur.e * NB + cur.nb_w) * KB + k] : 1.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float f = (group_act ? s_sa[k % kDStages][wm * 64 + i * 16 + (lane & 15)] : 1.0f) * sbv;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                bfr[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) acc[i][j][v] = acc[i][j][v] + t[v] * f;
+                        }
                     }
                 }
             }
@@ -566,14 +654,15 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a_q, const float* a_scale, in
         if (g > ceil_div(upper, 8) * 8) g = ceil_div(upper, 8) * 8;
         g = ceil_div(g < 8 ? 8 : g, 8) * 8;
         hipStream_t st = (hipStream_t)stream;
+        const uint8_t* no_e8m0 = nullptr;
         if (act_quant == MOE_ACT_PER_GROUP || w_quant == MOE_W_BLOCK)
-            hipLaunchKernelGGL(grouped_gemm_dma_kernel<true>, dim3((unsigned)g), dim3(kDThreads), 0, st,
-                               a_q, a_scale, act_quant, b_q, b_scale, w_quant, seg_indptr, num_local,
-                               m_cap, N, K, (uint16_t*)c_bf16);
+            hipLaunchKernelGGL((grouped_gemm_dma_kernel<true, false>), dim3((unsigned)g), dim3(kDThreads), 0, st,
+                               a_q, a_scale, act_quant, b_q, no_e8m0, b_scale, w_quant, seg_indptr,
+                               num_local, m_cap, N, K, (uint16_t*)c_bf16);
         else
-            hipLaunchKernelGGL(grouped_gemm_dma_kernel<false>, dim3((unsigned)g), dim3(kDThreads), 0, st,
-                               a_q, a_scale, act_quant, b_q, b_scale, w_quant, seg_indptr, num_local,
-                               m_cap, N, K, (uint16_t*)c_bf16);
+            hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, false>), dim3((unsigned)g), dim3(kDThreads), 0, st,
+                               a_q, a_scale, act_quant, b_q, no_e8m0, b_scale, w_quant, seg_indptr,
+                               num_local, m_cap, N, K, (uint16_t*)c_bf16);
         return launch_status();
     }
     const int64_t upper_tiles = (ceil_div(m_cap, BM) + num_local) * ceil_div(N, BN);
@@ -591,5 +680,37 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a_q, const float* a_scale, in
         hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s,
                            a_q, a_scale, act_quant, b_q, b_scale, w_quant, seg_indptr, num_local,
                            m_cap, N, K, (uint16_t*)c_bf16);
+    return launch_status();
+}
+
+extern "C" int moe_grouped_gemm_mxfp4(const uint8_t* a_q, const float* a_scale, int64_t a_scale_numel,
+                                      int32_t act_quant, const uint8_t* b_fp4, const uint8_t* b_e8m0,
+                                      const float* b_scale, int64_t b_scale_numel, int32_t w_quant,
+                                      const int32_t* seg_indptr, int32_t num_local, int64_t m_cap,
+                                      int32_t N, int32_t K, void* c_bf16, void* stream) {
+    using namespace moe;
+    if (num_local < 0 || m_cap < 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
+    if (act_quant < MOE_ACT_PER_TENSOR || act_quant > MOE_ACT_PER_GROUP) return MOE_ERR_INVALID_ARG;
+    if (w_quant < MOE_W_PER_EXPERT || w_quant > MOE_W_BLOCK) return MOE_ERR_INVALID_ARG;
+    if (act_quant == MOE_ACT_PER_GROUP || w_quant == MOE_W_BLOCK) return MOE_ERR_UNSUPPORTED;
+    if (K % DBK != 0 || N % 16 != 0 || num_local > kMaxLocal) return MOE_ERR_UNSUPPORTED;
+    if (m_cap > INT32_MAX / 2 || (int64_t)K * DBN >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+    const int64_t want_a = act_quant == MOE_ACT_PER_TENSOR ? 1 : m_cap;
+    const int64_t want_b = w_quant == MOE_W_PER_EXPERT ? num_local : (int64_t)num_local * N;
+    if (a_scale_numel != want_a || b_scale_numel != want_b) return MOE_ERR_SHAPE;
+    if (!seg_indptr) return MOE_ERR_NULL;
+    if (num_local == 0 || m_cap == 0) return MOE_OK;  // no rows can exist
+    if (!a_q || !a_scale || !b_fp4 || !b_e8m0 || !b_scale || !c_bf16) return MOE_ERR_NULL;
+    if (!aligned16(a_q) || !aligned16(b_fp4) || !aligned16(c_bf16) || ((uintptr_t)b_e8m0 & 3u) != 0)
+        return MOE_ERR_INVALID_ARG;
+
+    (void)hipGetLastError();
+    const int64_t upper = (ceil_div(m_cap, DBM) + num_local) * ceil_div(N, DBN);
+    int64_t g = (int64_t)device_cu_count();
+    if (g > ceil_div(upper, 8) * 8) g = ceil_div(upper, 8) * 8;
+    g = ceil_div(g < 8 ? 8 : g, 8) * 8;
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, true>), dim3((unsigned)g), dim3(kDThreads), 0,
+                       (hipStream_t)stream, a_q, a_scale, act_quant, b_fp4, b_e8m0, b_scale, w_quant,
+                       seg_indptr, num_local, m_cap, N, K, (uint16_t*)c_bf16);
     return launch_status();
 }

@@ -12,7 +12,8 @@ import dataclasses
 
 import torch
 
-from . import (moe_act_requant, moe_grouped_gemm_fp8, moe_post_reorder, moe_pre_reorder_quant,
+from . import (moe_act_requant, moe_grouped_gemm_fp8, moe_grouped_gemm_mxfp4, moe_post_reorder,
+               moe_pre_reorder_quant,
                moe_pre_reorder_quant_shared, moe_select_experts, moe_select_experts_shared,
                moe_workspace_bytes, ACT_PER_GROUP, ACT_PER_TENSOR, ACT_PER_TOKEN)
 
@@ -69,12 +70,14 @@ class LayerBuffers:
 def layer_forward(x, logits, correction_bias, w13, w13_scale, w2, w2_scale, buf: LayerBuffers, *,
                   topk, n_group, topk_group, score_fn, renormalize, routed_scaling_factor,
                   apply_rsf, expert_start, num_local, act_quant, w_quant, n_shared=0,
-                  shared_weight=1.0, stream=None):
+                  shared_weight=1.0, w13_e8m0=None, w2_e8m0=None, stream=None):
     """x bf16 [T,H], logits fp32 [T,E]; w13 e4m3 [E_l,2I,H]; w2 e4m3 [E_l,H,I]. Result in buf.out.
 
     With n_shared > 0 the shared experts are the last n_shared entries of w13 /
     w2 (E_l = num_local + n_shared) and every token also takes them with
-    weight shared_weight, inside the same grouped GEMMs."""
+    weight shared_weight, inside the same grouped GEMMs.
+    With w13_e8m0 / w2_e8m0 given, w13 / w2 are MXFP4 (packed E2M1 [E_l,N,K/2])
+    with those E8M0 block scales, and w13_scale / w2_scale the fp32 factors."""
     if n_shared:
         moe_select_experts_shared(logits, correction_bias, buf.topk_ids, buf.topk_weights,
                                   topk=topk, n_shared=n_shared, shared_weight=shared_weight,
@@ -95,11 +98,19 @@ def layer_forward(x, logits, correction_bias, w13, w13_scale, w2, w2_scale, buf:
         moe_pre_reorder_quant(x, buf.topk_ids, buf.a13, buf.a13_scale, buf.src2dst, buf.dst2src,
                               buf.seg_indptr, buf.workspace, expert_start=expert_start,
                               num_local=num_local, act_quant=act_quant, stream=stream)
-    moe_grouped_gemm_fp8(buf.a13, buf.a13_scale, w13, w13_scale, buf.seg_indptr, buf.c13,
-                         act_quant=act_quant, w_quant=w_quant, stream=stream)
+    if w13_e8m0 is not None:
+        moe_grouped_gemm_mxfp4(buf.a13, buf.a13_scale, w13, w13_e8m0, w13_scale, buf.seg_indptr, buf.c13,
+                               act_quant=act_quant, w_quant=w_quant, stream=stream)
+    else:
+        moe_grouped_gemm_fp8(buf.a13, buf.a13_scale, w13, w13_scale, buf.seg_indptr, buf.c13,
+                             act_quant=act_quant, w_quant=w_quant, stream=stream)
     moe_act_requant(buf.c13, buf.seg_indptr, buf.a2, buf.a2_scale, buf.workspace,
                     act_quant=act_quant, stream=stream)
-    moe_grouped_gemm_fp8(buf.a2, buf.a2_scale, w2, w2_scale, buf.seg_indptr, buf.c2,
-                         act_quant=act_quant, w_quant=w_quant, stream=stream)
+    if w2_e8m0 is not None:
+        moe_grouped_gemm_mxfp4(buf.a2, buf.a2_scale, w2, w2_e8m0, w2_scale, buf.seg_indptr, buf.c2,
+                               act_quant=act_quant, w_quant=w_quant, stream=stream)
+    else:
+        moe_grouped_gemm_fp8(buf.a2, buf.a2_scale, w2, w2_scale, buf.seg_indptr, buf.c2,
+                             act_quant=act_quant, w_quant=w_quant, stream=stream)
     moe_post_reorder(buf.c2, buf.src2dst, buf.topk_weights, buf.out, stream=stream)
     return buf.out

@@ -13,6 +13,7 @@
  *   moe_router_select      router projection (bf16 MFMA) + stage 1
  *   moe_select_experts_shared, moe_pre_reorder_quant_shared
  *                          shared experts fused as extra local experts
+ *   moe_grouped_gemm_mxfp4 stage 3 with MXFP4 expert weights
  *
  * Conventions shared by every call
  *   - C linkage; all tensors are device pointers to caller-owned memory,
@@ -216,6 +217,37 @@ int moe_grouped_gemm_fp8(const uint8_t* a_q, const float* a_scale, int64_t a_sca
                          int64_t b_scale_numel, int32_t w_quant, const int32_t* seg_indptr,
                          int32_t num_local, int64_t m_cap, int32_t N, int32_t K, void* c_bf16,
                          void* stream);
+
+/*
+ * Stage 3 (and 5) with FP4 expert weights.
+ * Source: "[1/2] sgl-kernel: Fuse routed scaling factor into select_experts"
+ * (sglang PR #8364), Summary of Changes and Highlights: the layer is run with
+ * FP4-quantised expert weights (an FP4 checkpoint in its benchmark commands).
+ * The pages do not define the encoding; this call takes OCP MXFP4, the format
+ * the gfx950 matrix cores consume natively.
+ *
+ * For every local expert e and row r in [seg_indptr[e], seg_indptr[e+1]):
+ *   C[r, n] = bf16( sa(r) * sb(e, n) * sum_k A[r,k] * e2m1(B[e,n,k]) * 2^(S[e,n,k/32] - 127) )
+ * accumulated in fp32.
+ *   a_q         e4m3 [m_cap, K]; rows >= M are ignored.
+ *   a_scale     fp32, indexed by ROW: numel 1 (per tensor) or m_cap (per token).
+ *               Per-group activation scales return MOE_ERR_UNSUPPORTED.
+ *   b_fp4       packed E2M1 codes [num_local, N, K/2]: element k of a row is
+ *               byte k/2, the low nibble for even k (bit 3 sign, bits 2..1
+ *               exponent with bias 1, bit 0 mantissa).
+ *   b_e8m0      uint8 E8M0 block scales [num_local, N, K/32], 2^(s - 127);
+ *               4-byte aligned.
+ *   b_scale     fp32 factor, numel num_local (per expert) or num_local*N (per
+ *               channel); MOE_W_BLOCK returns MOE_ERR_UNSUPPORTED.
+ *   seg_indptr  int32 [num_local+1] on the device, clamped to [0, m_cap].
+ *   c_bf16      bf16 [m_cap, N] out; only rows < M are written.
+ * K must be a multiple of 128 and N of 16 (MOE_ERR_UNSUPPORTED otherwise).
+ */
+int moe_grouped_gemm_mxfp4(const uint8_t* a_q, const float* a_scale, int64_t a_scale_numel,
+                           int32_t act_quant, const uint8_t* b_fp4, const uint8_t* b_e8m0,
+                           const float* b_scale, int64_t b_scale_numel, int32_t w_quant,
+                           const int32_t* seg_indptr, int32_t num_local, int64_t m_cap, int32_t N,
+                           int32_t K, void* c_bf16, void* stream);
 
 /*
  * Stage 4, SiLU-and-mul + dynamic FP8 requantisation of the w2 input.

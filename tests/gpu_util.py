@@ -190,3 +190,27 @@ def assert_sum_close(got_bits, ref_bits, abs_terms, n_terms, what="output", ulps
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = np.where(abs_terms > 0, excess / abs_terms, 0.0)
     return float(ratio.max()) if ratio.size else 0.0
+
+
+def fp4_abs_values(packed, e8m0):
+    """|value| (fp64) of MXFP4 weights [.., N, K/2] with E8M0 scales [.., N, K/32],
+    decoded with the oracle's E2M1 / E8M0 definitions."""
+    import oracle
+    table = np.array([abs(oracle.e2m1_value(c)) for c in range(16)])
+    packed = np.asarray(packed)
+    nib = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
+    nib[..., 0::2], nib[..., 1::2] = packed & 15, packed >> 4
+    scale = np.ldexp(1.0, np.asarray(e8m0).astype(np.int64) - 127)
+    return table[nib] * np.repeat(scale, 32, axis=-1)
+
+
+def run_gemm_fp4(a_q, a_scale, act_quant, b_fp4, b_e8m0, b_scale, w_quant, seg):
+    m_cap, K = a_q.shape
+    N = b_fp4.shape[1]
+    c = Guarded((m_cap, N), torch.bfloat16)
+    moe.moe_grouped_gemm_mxfp4(up(a_q), up(a_scale), up(b_fp4), up(b_e8m0),
+                               up(np.asarray(b_scale, np.float32).reshape(-1)), up(seg.astype(np.int32)),
+                               c.t, act_quant=act_quant, w_quant=w_quant)
+    torch.cuda.synchronize()
+    c.check("c")
+    return bf16_bits(c.t)

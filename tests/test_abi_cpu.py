@@ -182,3 +182,21 @@ def test_shared_entry_points_reject(lib):
     assert p(ns=65) == moe.MOE_ERR_INVALID_ARG
     assert p(ns=-1) == moe.MOE_ERR_INVALID_ARG
     assert p(m_cap=35, nsc=35) == moe.MOE_ERR_SHAPE         # m_cap < T * min(9, 9)
+
+
+def test_mxfp4_gemm_rejects(lib):
+    f = lib.moe_grouped_gemm_mxfp4
+    def call(act=1, w=0, a_n=64, b_n=4, m_cap=64, N=128, K=256, num_local=4, seg=FAKE, c=FAKE, e8=FAKE):
+        return f(FAKE, FAKE, a_n, act, FAKE, e8, FAKE, b_n, w, seg, num_local, m_cap, N, K, c, None)
+    assert call(act=1, a_n=4) == moe.MOE_ERR_SHAPE
+    assert call(w=1, b_n=4) == moe.MOE_ERR_SHAPE                 # per channel needs 4*128
+    assert call(act=2, a_n=128) == moe.MOE_ERR_UNSUPPORTED       # per-group activations
+    assert call(w=2) == moe.MOE_ERR_UNSUPPORTED                  # block fp32 weight scales
+    assert call(K=192) == moe.MOE_ERR_UNSUPPORTED                # K % 128
+    assert call(N=120) == moe.MOE_ERR_UNSUPPORTED
+    assert call(w=7) == moe.MOE_ERR_INVALID_ARG
+    assert call(seg=None) == moe.MOE_ERR_NULL
+    assert call(e8=None) == moe.MOE_ERR_NULL
+    assert call(e8=ctypes.c_void_p(0x10002)) == moe.MOE_ERR_INVALID_ARG  # scales need 4-byte alignment
+    assert call(c=ctypes.c_void_p(0x10008)) == moe.MOE_ERR_INVALID_ARG
+    assert call(num_local=0, b_n=0) == moe.MOE_OK

@@ -19,7 +19,7 @@ from tests import gpu_util as G
 from tests.test_oracle_layer import small_cfg as _small_cfg, LAYER_CASES as _LAYER_CASES
 from tests.test_oracle_shared import shared_cfg
 
-LAYER_CASES = _LAYER_CASES + ["small_shared", "small_shared_block"]
+LAYER_CASES = _LAYER_CASES + ["small_shared", "small_shared_block", "small_fp4", "small_fp4_ep"]
 
 
 def small_cfg(name):
@@ -27,6 +27,14 @@ def small_cfg(name):
         return shared_cfg()
     if name == "small_shared_block":
         return shared_cfg(W.ACT_PER_GROUP, W.W_BLOCK, apply_rsf=0)
+    if name == "small_fp4":  # MXFP4 weights, softmax, per-tensor activations, every expert local
+        return W.MoEConfig(name=name, T=40, H=256, I=128, E=8, topk=2, num_local=8,
+                           score_fn=W.SCORE_SOFTMAX, act_quant=W.ACT_PER_TENSOR,
+                           w_quant=W.W_PER_EXPERT, w_fp4=True)
+    if name == "small_fp4_ep":  # MXFP4 weights, grouped sigmoid, EP slice, per-channel factors
+        return W.MoEConfig(name=name, T=56, H=384, I=256, E=16, topk=4, num_local=6, expert_start=5,
+                           score_fn=W.SCORE_SIGMOID, n_group=4, topk_group=2, rsf=2.5, use_bias=True,
+                           act_quant=W.ACT_PER_TOKEN, w_quant=W.W_PER_CHANNEL, w_fp4=True)
     return _small_cfg(name)
 
 pytestmark = pytest.mark.gpu
@@ -46,7 +54,9 @@ def run_layer(inp, w13_dev=None, w2_dev=None):
                       routed_scaling_factor=cfg.rsf, apply_rsf=cfg.apply_rsf,
                       expert_start=cfg.expert_start, num_local=cfg.num_local,
                       act_quant=cfg.act_quant, w_quant=cfg.w_quant, n_shared=cfg.n_shared,
-                      shared_weight=cfg.shared_weight)
+                      shared_weight=cfg.shared_weight,
+                      w13_e8m0=G.up(inp.w13_e8m0) if inp.w13_e8m0 is not None else None,
+                      w2_e8m0=G.up(inp.w2_e8m0) if inp.w2_e8m0 is not None else None)
     torch.cuda.synchronize()
     return buf
 
@@ -118,7 +128,8 @@ def e4m3_ordinal(codes):
 
 
 @pytest.mark.parametrize("name", ["dsv3_decode_ep", "dsv3_prefill_ep", "skewed_block",
-                                  "dsv3_decode_ep_shared", "dsv3_prefill_ep_shared"])
+                                  "dsv3_decode_ep_shared", "dsv3_prefill_ep_shared",
+                                  "dsv3_decode_ep_fp4", "dsv3_prefill_ep_fp4"])
 def test_layer_full_size_sampled_tokens(name):
     """Full workload in the benchmark's launch configuration. Routing and
     permutation are compared in full. For sampled tokens (all of them at decode)
@@ -185,6 +196,9 @@ def test_layer_full_size_sampled_tokens(name):
 
     def w_abs(which, e, N, K):
         sc = np.abs(np.asarray(getattr(inp, which + "_scale")[e]).reshape(-1).astype(np.float64))
+        if cfg.w_fp4:
+            return G.fp4_abs_values(getattr(inp, which)[e], getattr(inp, which + "_e8m0")[e]) * (
+                sc[:, None] if cfg.w_quant == W.W_PER_CHANNEL else sc[0])
         codes = np.abs(table[getattr(inp, which)[e]])
         if cfg.w_quant == W.W_PER_CHANNEL:
             return codes * sc[:, None]

@@ -267,8 +267,9 @@ def gen_expert_weight(cfg: MoEConfig, which: str, e_local: int, seed: int = 0):
 
 
 # Magnitude ranks 0..7 of E2M1 codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6) are drawn
-# with these probabilities (a bell shape, like block-quantised Gaussian weights).
-FP4_RANK_P = np.array([0.20, 0.22, 0.20, 0.14, 0.10, 0.08, 0.04, 0.02])
+# with probabilities 10, 11, 10, 7, 5, 4, 2, 1 in 50 (a bell shape, like
+# block-quantised Gaussian weights), by indexing this table with a uniform byte.
+FP4_RANK_TABLE = np.repeat(np.arange(8, dtype=np.uint8), [10, 11, 10, 7, 5, 4, 2, 1])
 FP4_E8M0_BASE = 120  # block scales 2^(119..121 - 127)
 
 
@@ -284,7 +285,7 @@ def gen_expert_weight_fp4(cfg: MoEConfig, which: str, e_local: int, seed: int = 
     else:
         raise ValueError(which)
     g = rng(seed, tid, cfg.expert_start + e_local, 4)
-    rank = g.choice(8, size=(N, K), p=FP4_RANK_P).astype(np.uint8)
+    rank = FP4_RANK_TABLE[g.integers(0, len(FP4_RANK_TABLE), size=(N, K), dtype=np.uint8)]
     sign = g.integers(0, 2, size=(N, K), dtype=np.uint8)
     nib = rank | (sign << 3)
     packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
