@@ -621,6 +621,217 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
     }
 }
 
+// ---- FP4 weights, 256-deep K steps: 128 x 256 tiles, two-stage DMA ring ----
+//
+// With MXFP4 weights a 128-deep K step moves 64 bytes per weight row, half a
+// cache line; the CU's load path costs per line touched, so this kernel steps
+// K by 256: a stage holds A (128 rows x 256 bytes, chunk c of row r at
+// c ^ (r & 15)), B (256 rows x 128 bytes = 256 codes, the perm8 layout) and the
+// rows' eight E8M0 scales, 66 KB; two stages fit. The DMA of step k+1 is issued
+// at step k (the same lead in time as two 128-deep steps), each step waits for
+// all of its loads, and the epilogue stages through the slot that is idle
+// while the next tile's first step loads. Waves, MFMA operand order and
+// epilogue as in the 128 x 256 FP8 kernel; each step is two 128-deep MFMA
+// steps. Requires K % 256 == 0.
+constexpr int F4K = 256;
+constexpr int kF4StageA = DBM * F4K;                 // 32 KB
+constexpr int kF4StageB = DBN * F4K / 2;             // 32 KB
+constexpr int kF4StageS = DBN * F4K / 32;            // 2 KB
+constexpr int kF4Stage = kF4StageA + kF4StageB + kF4StageS;
+constexpr int kF4DmaA = kF4StageA / 1024 / 8;        // 4
+constexpr int kF4DmaB = kF4StageB / 1024 / 8;        // 4
+
+__device__ __forceinline__ int swz256(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+
+struct F4Tile {
+    int e, row0, row_end, n0, a_rows, b_rows;
+    const uint8_t* a_g;
+    const uint8_t* b_g;
+    const uint8_t* s_g;
+    uint32_t a_off[kF4DmaA], b_off[kF4DmaB], s_off;
+};
+
+__global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_fp4_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, int act_quant,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Be8, const float* __restrict__ sb,
+    int w_quant, const int32_t* __restrict__ seg_in, int num_local, int64_t m_cap, int N, int K,
+    uint16_t* __restrict__ C) {
+    __shared__ __align__(16) uint8_t lds[2 * kF4Stage];
+    __shared__ int s_seg[kMaxLocal + 1];
+    __shared__ int s_tstart[kMaxLocal + 1];
+    __shared__ int scan_scratch[17];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid >> 2, wn = wid & 3;
+    const int nk = K / F4K;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const void*)lds;
+
+    const int total = build_tile_table<DBM, DBN>(seg_in, num_local, m_cap, N, s_seg, s_tstart, scan_scratch);
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd_blocks = gridDim.x >> 3;
+    const int per_xcd = (total + 7) / 8;
+    const int lt_begin = xcd * per_xcd;
+    const int lt_end = lt_begin + per_xcd < total ? lt_begin + per_xcd : total;
+
+    auto setup = [&](int lt) {
+        const TileCoord tc = tile_coord<DBM, DBN>(lt, s_seg, s_tstart, num_local);
+        F4Tile t;
+        t.e = tc.e;
+        t.row0 = tc.row0;
+        t.row_end = tc.row_end;
+        t.n0 = tc.n0;
+        t.a_rows = tc.row_end - tc.row0;
+        t.b_rows = N - tc.n0 < DBN ? N - tc.n0 : DBN;
+        // A: instruction i of wave w fills rows 4 (4 w + i) + lane / 16 at
+        // position lane % 16 (global chunk (lane % 16) ^ (row & 15))
+#pragma unroll
+        for (int i = 0; i < kF4DmaA; ++i) {
+            const int r = (wid * kF4DmaA + i) * 4 + (lane >> 4);
+            const int g = r < t.a_rows ? r : t.a_rows - 1;
+            t.a_off[i] = (uint32_t)g * (uint32_t)K + (uint32_t)((((lane & 15) ^ (r & 15)) << 4));
+        }
+        // B: instruction i of wave w fills rows 8 (4 w + i) + lane / 8 at
+        // position lane % 8 (global chunk (lane % 8) ^ perm8(row))
+#pragma unroll
+        for (int i = 0; i < kF4DmaB; ++i) {
+            const int r = (wid * kF4DmaB + i) * 8 + (lane >> 3);
+            const int g = r < t.b_rows ? r : t.b_rows - 1;
+            t.b_off[i] = (uint32_t)g * (uint32_t)(K / 2) + (uint32_t)((((lane & 7) ^ perm8(r)) << 4));
+        }
+        // scales: wave w loads dword lane % 2 of rows 32 w + lane / 2
+        const int rs = wid * 32 + (lane >> 1);
+        t.s_off = (uint32_t)(rs < t.b_rows ? rs : t.b_rows - 1) * (uint32_t)(K / 32) + (uint32_t)((lane & 1) * 4);
+        t.a_g = A + (int64_t)t.row0 * K;
+        t.b_g = B + ((int64_t)t.e * N + t.n0) * (K / 2);
+        t.s_g = Be8 + ((int64_t)t.e * N + t.n0) * (K / 32);
+        return t;
+    };
+    auto issue = [&](const F4Tile& t, int k, int s) {  // DMA of K step k into stage s
+        const uint32_t st = lds0 + (uint32_t)(s * kF4Stage);
+        const uint8_t* ab = uniform_ptr(t.a_g + k * F4K);
+        const uint32_t la = __builtin_amdgcn_readfirstlane(st + wid * kF4DmaA * 1024);
+#pragma unroll
+        for (int i = 0; i < kF4DmaA; ++i) dma16(ab, t.a_off[i], la + i * 1024);
+        const uint8_t* bb = uniform_ptr(t.b_g + k * (F4K / 2));
+        const uint32_t lb = __builtin_amdgcn_readfirstlane(st + kF4StageA + wid * kF4DmaB * 1024);
+#pragma unroll
+        for (int i = 0; i < kF4DmaB; ++i) dma16(bb, t.b_off[i], lb + i * 1024);
+        dma4(uniform_ptr(t.s_g + k * (F4K / 32)), t.s_off,
+             __builtin_amdgcn_readfirstlane(st + kF4StageA + kF4StageB + wid * 256));
+    };
+
+    int lt = lt_begin + slot;
+    if (lt >= lt_end) return;  // the whole block has no tile
+
+    F4Tile cur = setup(lt);
+    issue(cur, 0, 0);
+
+    while (true) {
+        float srow[4], scol[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = cur.row0 + wm * 64 + i * 16 + (lane & 15);
+            srow[i] = act_quant == MOE_ACT_PER_TENSOR ? sa[0] : sa[r < cur.row_end ? r : cur.row0];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int n = cur.n0 + wn * 64 + j * 16 + (lane >> 4) * 4 + v;
+                scol[j][v] = w_quant == MOE_W_PER_EXPERT ? sb[cur.e] : sb[(int64_t)cur.e * N + (n < N ? n : N - 1)];
+            }
+
+        v4f acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+        for (int k = 0; k < nk; ++k) {
+            wait_vmcnt<0>();
+            __syncthreads();  // stage k complete; every wave is done with the other stage
+            if (k + 1 < nk) issue(cur, k + 1, (k + 1) & 1);
+
+            const uint8_t* la = lds + (k & 1) * kF4Stage;
+            const uint8_t* lb = la + kF4StageA;
+            const uint8_t* lsc = lb + kF4StageB;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {  // two 128-deep MFMA steps
+                v8i af[4], bfr[4];
+                int scl[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // activations in the order the scaled MFMA pairs with E2M1
+                    // lanes: chunks l/16 and l/16 + 4 of this 128-deep half
+                    const int r = wm * 64 + i * 16 + (lane & 15);
+                    const int c = h * 8 + (lane >> 4);
+                    const uint4 lo = *(const uint4*)(la + swz256(r, c));
+                    const uint4 hi = *(const uint4*)(la + swz256(r, c + 4));
+                    af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rb = wn * 64 + j * 16 + (lane & 15);
+                    const uint4 q = *(const uint4*)(lb + swz(rb, h * 4 + (lane >> 4)));
+                    bfr[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+                    scl[j] = (int)lsc[rb * 8 + h * 4 + (lane >> 4)];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bfr[j], af[i], acc[i][j], 4, 0, 0, scl[j], 0, 127);
+            }
+        }
+        __syncthreads();  // every wave is done with both stages
+
+        // the next tile's first step loads into stage 0 during this epilogue
+        const int lt_next = lt + per_xcd_blocks;
+        const bool has_next = lt_next < lt_end;
+        F4Tile nxt;
+        if (has_next) {
+            nxt = setup(lt_next);
+            issue(nxt, 0, 0);
+        }
+
+        // ---- epilogue through stage 1: scales, bf16, 16-byte row stores, two
+        // halves of 32 rows per wave ----
+        uint8_t* ep = lds + kF4Stage + wid * (32 * 128);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+                const int i = 2 * h + ii;
+                const int rl = ii * 16 + (lane & 15);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int cl = j * 16 + (lane >> 4) * 4;
+                    uint32_t hb[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) hb[v] = f32_to_bf16_bits(acc[i][j][v] * (srow[i] * scol[j][v]));
+                    *(uint2*)(ep + ep_off(rl, cl >> 3) + (cl & 7) * 2) =
+                        make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int rl = t * 8 + (lane >> 3), qc = lane & 7;
+                const int r = cur.row0 + wm * 64 + h * 32 + rl;
+                const int n = cur.n0 + wn * 64 + qc * 8;
+                const uint4 v = *(const uint4*)(ep + ep_off(rl, qc));
+                if (r < cur.row_end && n < N) *(uint4*)(C + (int64_t)r * N + n) = v;
+            }
+            __syncthreads();
+        }
+        if (!has_next) break;
+        cur = nxt;
+        lt = lt_next;
+    }
+    wait_vmcnt<0>();
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -709,8 +920,13 @@ extern "C" int moe_grouped_gemm_mxfp4(const uint8_t* a_q, const float* a_scale, 
     int64_t g = (int64_t)device_cu_count();
     if (g > ceil_div(upper, 8) * 8) g = ceil_div(upper, 8) * 8;
     g = ceil_div(g < 8 ? 8 : g, 8) * 8;
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, true>), dim3((unsigned)g), dim3(kDThreads), 0,
-                       (hipStream_t)stream, a_q, a_scale, act_quant, b_fp4, b_e8m0, b_scale, w_quant,
-                       seg_indptr, num_local, m_cap, N, K, (uint16_t*)c_bf16);
+    if (K % F4K == 0)  // full cache lines of weights per K step
+        hipLaunchKernelGGL(grouped_gemm_fp4_kernel, dim3((unsigned)g), dim3(kDThreads), 0,
+                           (hipStream_t)stream, a_q, a_scale, act_quant, b_fp4, b_e8m0, b_scale, w_quant,
+                           seg_indptr, num_local, m_cap, N, K, (uint16_t*)c_bf16);
+    else
+        hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, true>), dim3((unsigned)g), dim3(kDThreads), 0,
+                           (hipStream_t)stream, a_q, a_scale, act_quant, b_fp4, b_e8m0, b_scale, w_quant,
+                           seg_indptr, num_local, m_cap, N, K, (uint16_t*)c_bf16);
     return launch_status();
 }

@@ -45,7 +45,8 @@ def abs_products_fp4(a_q, sa, act_quant, b_fp4, b_e8m0, sb, w_quant, seg, rows):
 
 @pytest.mark.parametrize("act_quant,w_quant", [(W.ACT_PER_TENSOR, W.W_PER_EXPERT),
                                                (W.ACT_PER_TOKEN, W.W_PER_CHANNEL)])
-def test_mxfp4_gemm_exact_case(act_quant, w_quant):
+@pytest.mark.parametrize("K", [384, 768])  # 128-deep and 256-deep K steps
+def test_mxfp4_gemm_exact_case(act_quant, w_quant, K):
     """Activations in {-1, 0, 1}, weights in {0, +-0.5, +-1, +-2} times block
     scales 2^-1 or 2^0, and power-of-two factors: every product and partial sum
     is a multiple of 2^-2 below 2^10, exact in fp32 and inside the MFMA's
@@ -53,7 +54,7 @@ def test_mxfp4_gemm_exact_case(act_quant, w_quant):
     g = np.random.default_rng(11)
     counts = [70, 0, 129, 3]
     seg = _seg(counts)
-    m_cap, N, K = int(seg[-1]) + 5, 272, 384
+    m_cap, N = int(seg[-1]) + 5, 272
     E = len(counts)
     a_q = W.to_e4m3_codes(g.integers(-1, 2, size=(m_cap, K)).astype(np.float32))
     nib = np.array([0, 1, 2, 4, 9, 10, 12], np.uint8)[g.integers(0, 7, size=(E, N, K))]
@@ -61,7 +62,7 @@ def test_mxfp4_gemm_exact_case(act_quant, w_quant):
     b_e8m0 = g.integers(126, 128, size=(E, N, K // 32)).astype(np.uint8)
     sa = np.ldexp(1.0, g.integers(-2, 3, size=1 if act_quant == W.ACT_PER_TENSOR else m_cap)).astype(np.float32)
     sb = np.ldexp(1.0, g.integers(-2, 3, size=E if w_quant == W.W_PER_EXPERT else E * N)).astype(np.float32)
-    print(f"mxfp4 exact act={act_quant} w={w_quant}", flush=True)
+    print(f"mxfp4 exact act={act_quant} w={w_quant} K={K}", flush=True)
     ref = oracle.grouped_gemm_mxfp4(a_q, sa, act_quant, b_fp4, b_e8m0, sb, w_quant, seg)
     c = G.run_gemm_fp4(a_q, sa, act_quant, b_fp4, b_e8m0, sb, w_quant, seg)
     M = int(seg[-1])
