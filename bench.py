@@ -296,12 +296,14 @@ def time_router_select(cfg, inp, args, moe, W, torch, dev):
     logits = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=dev)
     ids = torch.empty(cfg.T, cfg.topk, dtype=torch.int32, device=dev)
     w = torch.empty(cfg.T, cfg.topk, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(moe.moe_router_workspace_bytes(cfg.T, cfg.H, cfg.E), 256), dtype=torch.uint8,
+                     device=dev)
 
     def run():
         moe.moe_router_select(x, wg, bias, logits, ids, w, topk=cfg.topk, n_group=cfg.n_group,
                               topk_group=cfg.topk_group, score_fn=cfg.score_fn,
                               renormalize=cfg.renormalize, routed_scaling_factor=cfg.rsf,
-                              apply_rsf=cfg.apply_rsf)
+                              apply_rsf=cfg.apply_rsf, workspace=ws)
     for _ in range(3):
         run()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -32,7 +32,7 @@ W_PER_EXPERT, W_PER_CHANNEL, W_BLOCK = 0, 1, 2
 EXPORTS = ["moe_select_experts", "moe_workspace_bytes", "moe_pre_reorder_quant",
            "moe_grouped_gemm_fp8", "moe_act_requant", "moe_post_reorder", "moe_status_string",
            "moe_router_select", "moe_select_experts_shared", "moe_pre_reorder_quant_shared",
-           "moe_grouped_gemm_mxfp4"]
+           "moe_grouped_gemm_mxfp4", "moe_router_workspace_bytes"]
 
 _lib = None
 
@@ -81,7 +81,9 @@ def load_library():
                                                  P, I64, P, P, P, P, SZ, P]
     lib.moe_router_select.restype = ctypes.c_int
     lib.moe_router_select.argtypes = [P, P, P, I64, I32, I32, I32, I32, I32, I32, I32, F32, I32, P, P,
-                                      P, P]
+                                      P, P, SZ, P]
+    lib.moe_router_workspace_bytes.restype = SZ
+    lib.moe_router_workspace_bytes.argtypes = [I64, I32, I32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -145,11 +147,17 @@ def moe_select_experts(logits, correction_bias, topk_ids, topk_weights, *, topk,
     _check(rc, "moe_select_experts")
 
 
+def moe_router_workspace_bytes(T: int, H: int, E: int) -> int:
+    return int(load_library().moe_router_workspace_bytes(T, H, E))
+
+
 def moe_router_select(x, wg, correction_bias, logits, topk_ids, topk_weights, *, topk, n_group=1,
                       topk_group=1, score_fn=SCORE_SOFTMAX, renormalize=1,
-                      routed_scaling_factor=1.0, apply_rsf=1, stream=None):
+                      routed_scaling_factor=1.0, apply_rsf=1, workspace=None, stream=None):
     """Router projection logits = x @ wg^T (x bf16 [T, H], wg bf16 [E, H]) into
-    `logits` (fp32 [T, E]), then stage 1 on them."""
+    `logits` (fp32 [T, E]), then stage 1 on them. `workspace`: a device byte
+    tensor of at least moe_router_workspace_bytes(T, H, E) (allocated here when
+    omitted)."""
     _dtype(x, torch.bfloat16, name="x")
     _dtype(wg, torch.bfloat16, name="wg")
     _dtype(correction_bias, torch.float32, name="correction_bias")
@@ -160,10 +168,14 @@ def moe_router_select(x, wg, correction_bias, logits, topk_ids, topk_weights, *,
     E = wg.shape[0]
     if wg.shape[1] != H or tuple(logits.shape) != (T, E):
         raise MoEError("moe_router_select: shapes of x, wg and logits disagree")
+    need = moe_router_workspace_bytes(T, H, E)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = load_library().moe_router_select(
         _ptr(x), _ptr(wg), _ptr(correction_bias), T, H, E, topk, n_group, topk_group, score_fn,
         renormalize, float(routed_scaling_factor), apply_rsf, _ptr(logits), _ptr(topk_ids),
-        _ptr(topk_weights), _stream(stream))
+        _ptr(topk_weights), _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "moe_router_select")
 
 

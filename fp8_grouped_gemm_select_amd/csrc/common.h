@@ -148,4 +148,39 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
     return res;
 }
 
+// ---- global -> LDS DMA (explicitly waited) ---------------------------------------
+
+// One 16-byte global -> LDS DMA per lane: from base + voff (base wave-uniform
+// in SGPRs, voff a per-lane 32-bit offset) to LDS address lds_base + 16 * lane
+// (lds_base wave-uniform, in M0). Inline assembly so that the compiler inserts
+// no waits of its own around it; every wait on these loads is explicit.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_base)
+                 : "memory");
+}
+
+// One 4-byte global -> LDS DMA per lane, to LDS address lds_base + 4 * lane.
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_base)
+                 : "memory");
+}
+
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t*)(((uint64_t)hi << 32) | lo);
+}
+
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt left alone
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
+
 }  // namespace moe

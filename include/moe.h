@@ -108,6 +108,10 @@ int moe_select_experts(const float* logits, const float* correction_bias, int64_
  *   moe_select_experts on them with the same stage-1 arguments.
  *   x_bf16   bf16 [T, H];  wg_bf16  bf16 [E, H] (one row per expert, the
  *            transpose of the [H, E] projection);  logits  fp32 [T, E] out.
+ *   workspace  device scratch of at least moe_router_workspace_bytes(T, H, E)
+ *            bytes, 16-byte aligned (split-K partial logits, summed in a fixed
+ *            order, so the logits are the same on every call); may be NULL
+ *            when that size is 0. Too small: MOE_ERR_WORKSPACE.
  * Limits: H % 8 == 0, E % 4 == 0, and those of moe_select_experts. A stage-1
  * argument error is reported before anything is enqueued.
  */
@@ -115,7 +119,11 @@ int moe_router_select(const void* x_bf16, const void* wg_bf16, const float* corr
                       int64_t T, int32_t H, int32_t E, int32_t topk, int32_t n_group,
                       int32_t topk_group, int32_t score_fn, int32_t renormalize,
                       float routed_scaling_factor, int32_t apply_rsf, float* logits,
-                      int32_t* topk_ids, float* topk_weights, void* stream);
+                      int32_t* topk_ids, float* topk_weights, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Workspace bytes moe_router_select needs for this shape (0 when it needs none). */
+size_t moe_router_workspace_bytes(int64_t T, int32_t H, int32_t E);
 
 /*
  * Shared-expert fusion (extension). The pages note that shared-expert fusion is

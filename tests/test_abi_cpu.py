@@ -152,8 +152,9 @@ def test_binding_keyword_only():
 
 def test_router_select_rejects(lib):
     f = lib.moe_router_select
-    def call(T=4, H=64, E=8, k=2, ng=1, tg=1, sf=0, x=FAKE, wg=FAKE, logits=FAKE, ids=FAKE):
-        return f(x, wg, None, T, H, E, k, ng, tg, sf, 1, 1.0, 1, logits, ids, FAKE, None)
+    def call(T=4, H=64, E=8, k=2, ng=1, tg=1, sf=0, x=FAKE, wg=FAKE, logits=FAKE, ids=FAKE, ws=None,
+             ws_bytes=0):
+        return f(x, wg, None, T, H, E, k, ng, tg, sf, 1, 1.0, 1, logits, ids, FAKE, ws, ws_bytes, None)
     assert call(H=12) == moe.MOE_ERR_UNSUPPORTED          # H % 8
     assert call(E=6) == moe.MOE_ERR_UNSUPPORTED           # E % 4
     assert call(E=0) == moe.MOE_ERR_INVALID_ARG
@@ -166,6 +167,21 @@ def test_router_select_rejects(lib):
     assert call(ng=3, sf=1) == moe.MOE_ERR_INVALID_ARG
     assert call(ids=None) == moe.MOE_ERR_NULL
     assert call(T=0) == moe.MOE_OK
+    # split-K shapes (H % 64 == 0, E % 64 == 0) need the workspace
+    need = lib.moe_router_workspace_bytes(4, 128, 64)
+    assert need == 4 * 64 * 4 * 2          # two K splits of [T, E] fp32 partials
+    assert call(H=128, E=64) == moe.MOE_ERR_WORKSPACE
+    assert call(H=128, E=64, ws=FAKE, ws_bytes=need - 4) == moe.MOE_ERR_WORKSPACE
+    assert call(H=128, E=64, ws=ctypes.c_void_p(0x10008), ws_bytes=need) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_router_workspace_sizes(lib):
+    f = lib.moe_router_workspace_bytes
+    assert f(8192, 7168, 256) == 4 * 8192 * 256 * 4     # 64 tiles x 4 splits fill 256 CUs
+    assert f(128, 7168, 256) == 16 * 128 * 256 * 4     # one tile: 16 splits of 7 steps
+    assert f(16, 120, 64) == 0                          # H % 64: the unsplit kernel
+    assert f(16, 128, 8) == 0                           # E % 64: the unsplit kernel
+    assert f(0, 128, 64) == 0
 
 
 def test_shared_entry_points_reject(lib):
