@@ -11,13 +11,14 @@
 //   count    a pair's stable rank among the chunk's earlier pairs of the same
 //            local expert (register compares, kept in src2dst) and the
 //            chunk's count per expert, stored expert-major [E_l][nchunks];
-//   scan     one block: a flat exclusive scan of those counts in expert-major
-//            order, so entry (e, c) is the first row of expert e's pairs from
-//            chunk c, and entry (e, 0) is seg_indptr[e]; per-tensor amax
-//            partials -> one scale;
+//   scan     one block per local expert: an exclusive scan of its chunk
+//            counts (entry (e, c) = expert e's pairs in chunks before c) and its
+//            total; block 0 also reduces the per-tensor amax partials;
 //   scatter  one wave per token: its row loads are issued as soon as its ids
-//            are known; final rows, dst2src, and the quantised row written to
-//            each of the token's local rows; the grid clears dst2src[M..m_cap).
+//            are known; the experts' first rows (seg_indptr) come from a wave
+//            prefix sum of the totals, block 0 writes them out; final rows,
+//            dst2src, and the quantised row written to each of the token's
+//            local rows; the grid clears dst2src[M..m_cap).
 #include "common.h"
 
 namespace moe {
@@ -29,7 +30,8 @@ constexpr int kAmaxBlocks = 1024;
 
 struct PreWs {
     int32_t* counts;   // [num_local][nchunks]
-    int32_t* offs;     // [num_local][nchunks], exclusive scan of counts
+    int32_t* offs;     // [num_local][nchunks], exclusive scan of counts within each expert
+    int32_t* tot;      // [num_local], pairs per local expert
     float* amax_part;  // [kAmaxBlocks]
     float* tscale;     // [2]: per-tensor scale, inverse
 };
@@ -38,7 +40,7 @@ __host__ __device__ inline size_t align256(size_t b) { return (b + 255) & ~(size
 
 inline int64_t n_chunks(int64_t T, int32_t topk) { return ceil_div(T * (int64_t)topk, kChunkPairs); }
 
-// counts / offs entries, padded so that the scan's 16-byte loads stay inside
+// counts / offs entries (padded to a multiple of 32, plus 32)
 inline int64_t n_entries(int64_t T, int32_t topk, int32_t num_local) {
     return (n_chunks(T, topk) * num_local + 31) / 32 * 32 + 32;
 }
@@ -48,6 +50,7 @@ inline size_t pre_ws_bytes(int64_t T, int32_t topk, int32_t num_local) {
     size_t b = 0;
     b += align256(sizeof(int32_t) * (size_t)ne);
     b += align256(sizeof(int32_t) * (size_t)ne);
+    b += align256(sizeof(int32_t) * (size_t)(num_local > 0 ? num_local : 1));
     b += align256(sizeof(float) * kAmaxBlocks);
     b += align256(sizeof(float) * 2);
     return b;
@@ -61,6 +64,8 @@ inline PreWs pre_ws_carve(void* ws, int64_t T, int32_t topk, int32_t num_local) 
     p += align256(sizeof(int32_t) * (size_t)ne);
     w.offs = (int32_t*)p;
     p += align256(sizeof(int32_t) * (size_t)ne);
+    w.tot = (int32_t*)p;
+    p += align256(sizeof(int32_t) * (size_t)(num_local > 0 ? num_local : 1));
     w.amax_part = (float*)p;
     p += align256(sizeof(float) * kAmaxBlocks);
     w.tscale = (float*)p;
@@ -130,70 +135,82 @@ __global__ __launch_bounds__(256) void pr_amax_kernel(const uint4* __restrict__ 
     if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// ---- scan: flat exclusive scan of the expert-major counts ---------------------------
-// 1024 threads, in passes of 1024 x 32 entries: thread t loads its 32 contiguous
-// entries of the pass at once (8 x 16 bytes), the block scans the thread sums,
-// and the running carry joins the passes. The workspace rows are padded to a
-// multiple of 32 entries past n (zero counts), so the vector loads stay inside.
-constexpr int kScanPer = 32;
-__global__ __launch_bounds__(1024) void pr_scan_kernel(const int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ offs, int64_t nch,
-                                                       int num_local, int32_t* __restrict__ seg,
-                                                       const float* __restrict__ amax_part,
-                                                       int n_part, int per_tensor,
-                                                       float* __restrict__ a_scale,
-                                                       float* __restrict__ tscale) {
+// ---- scan: per-expert exclusive scans of the chunk counts ------------------------------
+// Block e scans row e of the expert-major counts in passes of 256 x 4 entries
+// and stores the row total; the experts' first rows are prefix sums of those
+// totals, formed where they are used (expert_base below). Block 0 also reduces
+// the per-tensor amax partials into the scale and its inverse.
+__global__ __launch_bounds__(256) void pr_scan_kernel(const int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offs, int64_t nch,
+                                                      int num_local, int32_t* __restrict__ tot,
+                                                      const float* __restrict__ amax_part,
+                                                      int n_part, int per_tensor,
+                                                      float* __restrict__ a_scale,
+                                                      float* __restrict__ tscale) {
     __shared__ int scratch[17];
-    __shared__ float red[16];
+    __shared__ float red[4];
     const int tid = threadIdx.x;
-    const int64_t n = (int64_t)num_local * nch;
-    int carry = 0;
-    for (int64_t base = 0; base < n; base += 1024 * kScanPer) {
-        const int64_t i0 = base + (int64_t)tid * kScanPer;
-        int v[kScanPer];
+    const int e = blockIdx.x;
+    if (e < num_local) {
+        const int32_t* row = counts + (int64_t)e * nch;
+        int32_t* orow = offs + (int64_t)e * nch;
+        int carry = 0;
+        for (int64_t c0 = 0; c0 < nch; c0 += 256 * 4) {
+            int v[4];
+            int mine = 0;
 #pragma unroll
-        for (int q = 0; q < kScanPer / 4; ++q) {
-            int4 w = make_int4(0, 0, 0, 0);
-            if (i0 + 4 * q < n) w = *(const int4*)(counts + i0 + 4 * q);
-            v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+            for (int q = 0; q < 4; ++q) {
+                const int64_t c = c0 + tid * 4 + q;
+                v[q] = c < nch ? row[c] : 0;
+                mine += v[q];
+            }
+            int total = 0;
+            int run = carry + block_exclusive_scan(mine, scratch, &total);
+            carry += total;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t c = c0 + tid * 4 + q;
+                if (c < nch) orow[c] = run;
+                run += v[q];
+            }
         }
-        int mine = 0;
-#pragma unroll
-        for (int q = 0; q < kScanPer; ++q) mine += (i0 + q < n) ? v[q] : 0;
-        int total = 0;
-        int run = carry + block_exclusive_scan(mine, scratch, &total);
-        carry += total;
-        int o[kScanPer];
-#pragma unroll
-        for (int q = 0; q < kScanPer; ++q) {
-            o[q] = run;
-            run += (i0 + q < n) ? v[q] : 0;
-        }
-#pragma unroll
-        for (int q = 0; q < kScanPer / 4; ++q)
-            if (i0 + 4 * q < n) *(int4*)(offs + i0 + 4 * q) = make_int4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        if (tid == 0) tot[e] = carry;
     }
-    __syncthreads();  // offs written by the block is visible to all of it
-    for (int e = tid; e < num_local && nch > 0; e += 1024) seg[e] = offs[(int64_t)e * nch];
-    if (tid == 0) seg[num_local] = carry;
-    if (nch == 0)
-        for (int e = tid; e < num_local; e += 1024) seg[e] = 0;
-    if (per_tensor) {
+    if (e == 0 && per_tensor) {
         float m = 0.0f;
-        for (int i = tid; i < n_part; i += 1024) m = fmaxf(m, amax_part[i]);
+        for (int i = tid; i < n_part; i += 256) m = fmaxf(m, amax_part[i]);
         m = wave_max(m);
         if ((tid & 63) == 0) red[tid >> 6] = m;
         __syncthreads();
         if (tid == 0) {
-            float a = 0.0f;
-            for (int i = 0; i < 16; ++i) a = fmaxf(a, red[i]);
-            float s, inv;
-            dyn_scale(a, s, inv);
-            a_scale[0] = s;
-            tscale[0] = s;
+            const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            float sc, inv;
+            dyn_scale(a, sc, inv);
+            a_scale[0] = sc;
+            tscale[0] = sc;
             tscale[1] = inv;
         }
     }
+}
+
+// First row of local expert e (exclusive prefix sum of the totals, for each
+// lane's own e; lanes with e < 0 get 0) and, in `total`, M = all local pairs.
+// Wave-uniform loop over the totals in groups of 64.
+__device__ __forceinline__ int expert_base(const int32_t* __restrict__ tot, int num_local, int e, int lane,
+                                           int& total) {
+    int base = 0, carry = 0;
+    for (int q0 = 0; q0 < num_local; q0 += 64) {
+        const int v = q0 + lane < num_local ? tot[q0 + lane] : 0;
+        const int incl = wave_inclusive_scan(v, lane);
+        const int excl = incl - v + carry;
+        const int src = e - q0;
+        const bool here = src >= 0 && src < 64;
+        const int b = __shfl(excl, here ? src : 0, MOE_WAVE);
+        if (here) base = b;
+        carry += __shfl(incl, 63, MOE_WAVE);
+    }
+    total = carry;
+    return base;
 }
 
 // ---- scatter + quantise ------------------------------------------------------------------
@@ -218,7 +235,8 @@ __device__ __forceinline__ uint4 quant16(const uint4& a, const uint4& b, float i
 template <int MODE>
 __device__ __forceinline__ void scatter_token(
     const uint4* __restrict__ x, const int32_t* __restrict__ ids, int64_t t, int H, int topk,
-    const LocalMap& map, int64_t nch, const int32_t* __restrict__ offs,
+    const LocalMap& map, int num_local, int64_t nch, const int32_t* __restrict__ offs,
+    const int32_t* __restrict__ tot,
     int32_t* __restrict__ src2dst, int32_t* __restrict__ dst2src, uint8_t* __restrict__ a_q,
     float* __restrict__ a_scale, const float* __restrict__ tscale, int64_t m_cap, int lane) {
     const int64_t f = t * topk + lane;
@@ -260,9 +278,11 @@ __device__ __forceinline__ void scatter_token(
         }
     }
 
+    int m_all = 0;
+    const int base = expert_base(tot, num_local, e, lane, m_all);
     int dst = -1;
     if (e >= 0) {
-        dst = offs[(int64_t)e * nch + f / kChunkPairs] + src2dst[f];
+        dst = base + offs[(int64_t)e * nch + f / kChunkPairs] + src2dst[f];
         // rows past m_cap exist only if a token repeats an expert; drop them
         if (dst >= m_cap) dst = -1;
         else dst2src[dst] = (int32_t)f;
@@ -339,14 +359,27 @@ template <int MODE>
 __global__ __launch_bounds__(256) void pr_scatter_quant_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ ids, int64_t T, int H, int topk,
     LocalMap map, int num_local, int64_t nch, const int32_t* __restrict__ offs,
-    const int32_t* __restrict__ seg, int32_t* __restrict__ src2dst, int32_t* __restrict__ dst2src,
+    const int32_t* __restrict__ tot, int32_t* __restrict__ seg, int32_t* __restrict__ src2dst,
+    int32_t* __restrict__ dst2src,
     uint8_t* __restrict__ a_q, float* __restrict__ a_scale, const float* __restrict__ tscale,
     int64_t m_cap) {
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + wid;
-    const int64_t M = seg[num_local];  // needed only for the tail below
+    int m_all = 0;
+    expert_base(tot, num_local, -1, lane, m_all);  // M, for the tail below
+    const int64_t M = m_all;
+    if (blockIdx.x == 0 && wid == 0) {  // seg_indptr = [first rows..., M]
+        int carry = 0;
+        for (int q0 = 0; q0 < num_local; q0 += 64) {
+            const int v = q0 + lane < num_local ? tot[q0 + lane] : 0;
+            const int incl = wave_inclusive_scan(v, lane);
+            if (q0 + lane < num_local) seg[q0 + lane] = incl - v + carry;
+            carry += __shfl(incl, 63, MOE_WAVE);
+        }
+        if (lane == 0) seg[num_local] = carry;
+    }
     if (t < T)
-        scatter_token<MODE>(x, ids, t, H, topk, map, nch, offs, src2dst, dst2src,
+        scatter_token<MODE>(x, ids, t, H, topk, map, num_local, nch, offs, tot, src2dst, dst2src,
                             a_q, a_scale, tscale, m_cap, lane);
     // rows M .. m_cap-1 of dst2src are -1 (grid-stride over the whole grid)
     for (int64_t r = M + (int64_t)blockIdx.x * 256 + threadIdx.x; r < m_cap; r += (int64_t)gridDim.x * 256)
@@ -412,15 +445,17 @@ static int pre_reorder_impl(const void* x_bf16, const int32_t* topk_ids, int64_t
         hipLaunchKernelGGL(pr_amax_kernel, dim3(n_part), dim3(256), 0, s, (const uint4*)x_bf16,
                            n16, ws.amax_part);
     }
-    hipLaunchKernelGGL(pr_scan_kernel, dim3(1), dim3(1024), 0, s, ws.counts, ws.offs, nch,
-                       num_local, seg_indptr, ws.amax_part, n_part, per_tensor, a_scale, ws.tscale);
-    // The scatter grid also clears dst2src[M..m_cap); give it at least one block.
+    hipLaunchKernelGGL(pr_scan_kernel, dim3((unsigned)(num_local > 0 ? num_local : 1)), dim3(256), 0, s,
+                       ws.counts, ws.offs, nch, num_local, ws.tot, ws.amax_part, n_part, per_tensor,
+                       a_scale, ws.tscale);
+    // The scatter grid also writes seg_indptr and clears dst2src[M..m_cap); it
+    // always runs, with at least one block.
     const int64_t nblk = ceil_div(T, 4) > 0 ? ceil_div(T, 4) : 1;
-    if (m_cap > 0 || T > 0) {
+    {
 #define MOE_LAUNCH_SCATTER(MODE)                                                                  \
     hipLaunchKernelGGL(pr_scatter_quant_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s,     \
                        (const uint4*)x_bf16, topk_ids, T, H, topk, map, num_local, nch,          \
-                       ws.offs, seg_indptr, src2dst, dst2src, a_q, a_scale, ws.tscale, m_cap)
+                       ws.offs, ws.tot, seg_indptr, src2dst, dst2src, a_q, a_scale, ws.tscale, m_cap)
         if (act_quant == MOE_ACT_PER_TENSOR) MOE_LAUNCH_SCATTER(MOE_ACT_PER_TENSOR);
         else if (act_quant == MOE_ACT_PER_TOKEN) MOE_LAUNCH_SCATTER(MOE_ACT_PER_TOKEN);
         else MOE_LAUNCH_SCATTER(MOE_ACT_PER_GROUP);
