@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kRThreads) void router_logits_kernel(const uint16_t
 // blocks per 32-deep slice, issued W x X as above. x and wg rows of one
 // 64-element K step (128 bytes) go straight to LDS by global_load_lds_dwordx4
 // into a three-stage ring (the perm8 layout), loads of step k+2 issued at step
-// k with explicit waits. Requires H % 64 == 0; rows past T or E re-read the
+// k after its MFMAs, with explicit waits. Requires H % 64 == 0; rows past T or E re-read the
 // last valid row and are not stored.
 constexpr int SRM = 128, SRN = 256, SRK = 64;
 constexpr int kSRThreads = 512;
@@ -186,7 +186,6 @@ __global__ __launch_bounds__(kSRThreads, 1) void router_splitk_kernel(const uint
         if (k + 1 < nk) wait_vmcnt<kSRDma>();  // DMA(k) done; DMA(k+1) may be in flight
         else wait_vmcnt<0>();
         __syncthreads();  // stage k complete; every wave is done with stage k-1
-        if (k + 2 < nk) issue(k + 2);
         const uint8_t* lx = lds + (k % kSRStages) * kSRStage;
         const uint8_t* lw = lx + kSRStageA;
 #pragma unroll
@@ -203,6 +202,10 @@ __global__ __launch_bounds__(kSRThreads, 1) void router_splitk_kernel(const uint
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
         }
+        // the DMA of step k+2 after this step's MFMAs (into the stage read at step
+        // k-1, free since the barrier above)
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + 2 < nk) issue(k + 2);
     }
     // acc[i][j][v]: token t0 + 64 wm + 16 i + lane % 16, expert e0 + 64 wn + 16 j + 4 (lane / 16) + v
     float* out = part + (int64_t)split * T * E;
