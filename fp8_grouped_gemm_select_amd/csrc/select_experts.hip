@@ -68,14 +68,24 @@ __global__ __launch_bounds__(256) void select_experts_kernel(
     float key[EPL], sc[EPL];
     bool ok[EPL];
     float lmax = -INFINITY;
+    // all of the lane's logits and biases are loaded before any is used (indices
+    // clamped into the row, values past E masked below): one memory round trip
+    float lraw[EPL], braw[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane * EPL + i;
+        const int ec = e < E ? e : E - 1;
+        lraw[i] = l[ec];
+        braw[i] = bias ? bias[ec] : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane * EPL + i;
         ok[i] = active && e < E;
-        const float lv = ok[i] ? l[e] : 0.0f;
+        const float lv = ok[i] ? lraw[i] : 0.0f;
         if (score_fn == MOE_SCORE_SIGMOID) {
             sc[i] = sigmoid_fixed(lv);
-            key[i] = bias ? sc[i] + (ok[i] ? bias[e] : 0.0f) : sc[i];
+            key[i] = bias ? sc[i] + (ok[i] ? braw[i] : 0.0f) : sc[i];
         } else {
             sc[i] = lv;
             key[i] = lv;
