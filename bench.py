@@ -39,7 +39,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-next-rows", action="store_true",
-                   help="skip the separately timed extension rows (router projection)")
+                   help="skip the separately timed extension rows (router projection, FP4 layer) "
+                        "and the decode-share layer")
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
                    help="tokens in the oracle's timed sample (0: per-workload default)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -244,6 +245,10 @@ def main():
 
     if not args.no_next_rows:
         result["next_rows"] = {"router_select": time_router_select(cfg, inp, args, moe, W, torch, dev)}
+        if cfg.name == "dsv3_prefill_ep":  # context: the same layer's decode share
+            result["other_workloads"] = {"dsv3_decode_ep": time_other_layer(
+                W.CONFIGS["dsv3_decode_ep"], args, moe, W, torch, dev,
+                "the same layer at the decode share (T=128), timed on its own; not in value")}
         fp4_name = cfg.name + "_fp4"
         if not cfg.w_fp4 and fp4_name in W.CONFIGS:
             del buf
@@ -267,13 +272,19 @@ def main():
 
 def time_fp4_layer(cfg, args, moe, W, torch, dev):
     """The same layer with MXFP4 expert weights, timed on its own (not in `value`)."""
+    return time_other_layer(cfg, args, moe, W, torch, dev,
+                            "MXFP4 expert weights (E2M1 + E8M0 per 32), same routing and activations; not in value")
+
+
+def time_other_layer(cfg, args, moe, W, torch, dev, note):
+    """Another workload's whole layer, timed on its own (not in `value`)."""
     inp = W.gen_layer_inputs(cfg, seed=args.seed)
     ms, stage_ms, buf, s13, s2 = time_layer(cfg, inp, args.steps, args.warmup, moe, torch, dev)
     seg = buf.seg_indptr.cpu().numpy()
     work, M, _ = algorithmic_work(cfg, seg, buf.a13_scale.numel() * 4, buf.a2_scale.numel() * 4,
                                   s13.numel(), s2.numel())
     out = dict(workload=cfg.name, tokens_per_s=round(cfg.T / (ms * 1e-3), 1), ms_per_step=round(ms, 4),
-               note="MXFP4 expert weights (E2M1 + E8M0 per 32), same routing and activations; not in value")
+               M=int(M), note=note)
     for name in ("gemm_w13", "gemm_w2"):
         t = stage_ms[name] * 1e-3
         out[name] = dict(us=round(stage_ms[name] * 1e3, 2),
