@@ -81,11 +81,13 @@ def algorithmic_work(cfg, seg, a_scale_bytes13, a_scale_bytes2, w13_scale_numel,
 STAGES = ["select", "pre_reorder", "gemm_w13", "act_requant", "gemm_w2", "post_reorder"]
 
 
-def time_layer(cfg, inp, steps, warmup, moe, torch, dev):
+def time_layer(cfg, inp, steps, warmup, moe, torch, dev, graph=False):
     """Upload one workload's inputs, run `warmup` untimed layer passes, then time
     exactly `steps` passes (wall clock between synchronisations) with HIP events
     between the stages on the launch stream. Returns (ms per step, mean ms per
-    stage, the layer buffers, the two weight-scale tensors)."""
+    stage, the layer buffers, the two weight-scale tensors). With graph=True the
+    pass is captured once in a HIP graph and the timed steps are replays
+    (per-stage times are then None)."""
     def up(a, dtype=None):
         t = torch.from_numpy(np.ascontiguousarray(a))
         if dtype is not None:
@@ -153,6 +155,17 @@ def time_layer(cfg, inp, steps, warmup, moe, torch, dev):
         mark(5)
         moe.moe_post_reorder(buf.c2, buf.src2dst, buf.topk_weights, buf.out)
         mark(6)
+
+    if graph:
+        g = moe.LayerGraph(step, warmup=max(warmup, 1))
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t_start) * 1e3 / steps, None, buf, s13, s2
 
     for _ in range(warmup):
         step()
@@ -248,7 +261,7 @@ def main():
         if cfg.name == "dsv3_prefill_ep":  # context: the same layer's decode share
             result["other_workloads"] = {"dsv3_decode_ep": time_other_layer(
                 W.CONFIGS["dsv3_decode_ep"], args, moe, W, torch, dev,
-                "the same layer at the decode share (T=128), timed on its own; not in value")}
+                "the same layer at the decode share (T=128), timed on its own; not in value", graph=True)}
         fp4_name = cfg.name + "_fp4"
         if not cfg.w_fp4 and fp4_name in W.CONFIGS:
             del buf
@@ -276,15 +289,22 @@ def time_fp4_layer(cfg, args, moe, W, torch, dev):
                             "MXFP4 expert weights (E2M1 + E8M0 per 32), same routing and activations; not in value")
 
 
-def time_other_layer(cfg, args, moe, W, torch, dev, note):
-    """Another workload's whole layer, timed on its own (not in `value`)."""
+def time_other_layer(cfg, args, moe, W, torch, dev, note, graph=False):
+    """Another workload's whole layer, timed on its own (not in `value`); with
+    graph=True also replayed from a HIP graph."""
     inp = W.gen_layer_inputs(cfg, seed=args.seed)
+    ms_graph = None
+    if graph:
+        ms_graph, _, gbuf, _, _ = time_layer(cfg, inp, args.steps, args.warmup, moe, torch, dev, graph=True)
+        del gbuf
     ms, stage_ms, buf, s13, s2 = time_layer(cfg, inp, args.steps, args.warmup, moe, torch, dev)
     seg = buf.seg_indptr.cpu().numpy()
     work, M, _ = algorithmic_work(cfg, seg, buf.a13_scale.numel() * 4, buf.a2_scale.numel() * 4,
                                   s13.numel(), s2.numel())
     out = dict(workload=cfg.name, tokens_per_s=round(cfg.T / (ms * 1e-3), 1), ms_per_step=round(ms, 4),
                M=int(M), note=note)
+    if ms_graph is not None:  # the same pass replayed from a HIP graph (no per-launch host cost)
+        out["graph"] = dict(tokens_per_s=round(cfg.T / (ms_graph * 1e-3), 1), ms_per_step=round(ms_graph, 4))
     for name in ("gemm_w13", "gemm_w2"):
         t = stage_ms[name] * 1e-3
         out[name] = dict(us=round(stage_ms[name] * 1e3, 2),

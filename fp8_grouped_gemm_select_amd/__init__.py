@@ -290,4 +290,4 @@ def moe_post_reorder(down, src2dst, topk_weights, out, *, stream=None):
     _check(rc, "moe_post_reorder")
 
 
-from .layer import LayerBuffers, layer_forward  # noqa: E402
+from .layer import LayerBuffers, LayerGraph, layer_forward  # noqa: E402

@@ -114,3 +114,29 @@ def layer_forward(x, logits, correction_bias, w13, w13_scale, w2, w2_scale, buf:
                              act_quant=act_quant, w_quant=w_quant, stream=stream)
     moe_post_reorder(buf.c2, buf.src2dst, buf.topk_weights, buf.out, stream=stream)
     return buf.out
+
+
+class LayerGraph:
+    """One layer pass captured in a HIP graph (torch.cuda.CUDAGraph) for replay.
+
+    `fn` enqueues the pass (e.g. a closure over layer_forward with fixed
+    tensors); it runs `warmup` times on a side stream of default priority first
+    (the library caches device attributes on its first call), then once under
+    capture. Every replay reuses the captured device addresses, so the inputs
+    are updated in place between replays. The library enqueues no memset, copy
+    or allocation, so the graph holds only its kernels."""
+
+    def __init__(self, fn, warmup: int = 2):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            fn()
+
+    def replay(self):
+        self.graph.replay()
