@@ -303,11 +303,22 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void grouped_gemm_kernel(
 // each owns 64 x 64 outputs (4 x 4 MFMA 16x16x128). Operands go from memory to
 // LDS with global_load_lds_dwordx4 (no register staging): a stage holds the A
 // tile (128 rows) and the B tile (256 rows) of one 128-byte K step, in the same
-// perm8-swizzled row layout as above. The loads of step k+2 are issued at step
-// k; each wave waits only for its own loads of the step it is about to read,
-// then one barrier per step publishes the stage. Requires K % 128 == 0 (every
-// stage is whole; no zero fill). Rows past the valid range re-read the last
-// valid row, so every wave issues the same loads every step.
+// perm8-swizzled row layout as above. Each wave waits only for its own loads
+// of the step it is about to read, then one barrier per step publishes the
+// stage. Requires K % 128 == 0 (every stage is whole; no zero fill). Rows past
+// the valid range re-read the last valid row, so every wave issues the same
+// loads every step.
+//
+// Plain FP8 path (scales constant along K): the operands of step k+1 are read
+// from LDS into a second register set while step k's MFMAs run (one operand
+// read per two MFMAs), and the six DMA instructions of step k+3 go out one per
+// MFMA pair into the slot step k has just left. After the barrier of a step
+// the matrix core has its operands at once; the loads no longer queue behind
+// one another at the end of the step. The tile's epilogue scales (128 row and
+// 256 column values) arrive in LDS by 4-byte DMA with its first step, so no
+// registers hold them during the K loop. Other paths (K-dependent scales,
+// FP4 weights): operands read after the barrier, DMA of step k+2 issued
+// before the reads.
 constexpr int DBM = 128, DBN = 256, DBK = 128;
 constexpr int kDThreads = 512;
 constexpr int kDStages = 3;
@@ -353,6 +364,9 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
     __shared__ int s_tstart[kMaxLocal + 1];
     __shared__ int scan_scratch[17];
     __shared__ float s_sa[kDStages][DBM];
+    // epilogue scales of a tile on the register-prefetch path: sa of its 128
+    // rows, then sb of its 256 columns; two buffers, tiles alternate
+    __shared__ __align__(16) float s_scale[2][DBM + DBN];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -442,6 +456,24 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
         }
     };
 
+    // Epilogue scales of tile t into s_scale[p] by 4-byte DMA (plain FP8 path):
+    // waves 0-1 the rows' sa, waves 2-5 the columns' sb (indices clamped).
+    const uint32_t lds_scale = (uint32_t)(uintptr_t)(const void*)&s_scale[0][0];
+    auto issue_scales = [&](const DTile& t, int p) {
+        if (wid < 2) {
+            const int r = wid * 64 + lane;
+            const int g = t.row0 + (r < t.a_rows ? r : t.a_rows - 1);
+            const uint32_t off = act_quant == MOE_ACT_PER_TENSOR ? 0u : (uint32_t)g * 4u;
+            dma4((const uint8_t*)sa, off, __builtin_amdgcn_readfirstlane(lds_scale + (uint32_t)(p * (DBM + DBN) + wid * 64) * 4u));
+        } else if (wid < 6) {
+            const int c = (wid - 2) * 64 + lane;
+            const int n = t.n0 + c < N ? t.n0 + c : N - 1;
+            const uint32_t off = w_quant == MOE_W_PER_EXPERT ? (uint32_t)t.e * 4u : (uint32_t)((int64_t)t.e * N + n) * 4u;
+            dma4((const uint8_t*)sb, off, __builtin_amdgcn_readfirstlane(lds_scale + (uint32_t)(p * (DBM + DBN) + DBM + c - lane) * 4u));
+        }
+    };
+    int par = 0;  // s_scale buffer of the current tile
+
     int lt = lt_begin + slot;
     if (lt >= lt_end) return;  // the whole block has no tile
 
@@ -455,12 +487,25 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
     DTile cur = setup(lt);
     float q = 0.f;
     if (group_act) q = sa[(int64_t)cur.sa_row * KB];
+    if constexpr (!FP4 && !KDEP) issue_scales(cur, par);
     issue(cur, 0);
     if (nk > 1) issue(cur, 1);
 
     while (true) {
-        // epilogue scales of this tile, in flight during the K loop
+        // epilogue scales of this tile (in flight during the K loop, except on the
+        // register-prefetch path, which needs the registers)
         float srow[4], scol[4][4];
+        auto load_scales = [&]() {
+            if constexpr (!FP4 && !KDEP) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) srow[i] = s_scale[par][wm * 64 + i * 16 + (lane & 15)];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float4 v4 = *(const float4*)&s_scale[par][DBM + wn * 64 + j * 16 + (lane >> 4) * 4];
+                    scol[j][0] = v4.x; scol[j][1] = v4.y; scol[j][2] = v4.z; scol[j][3] = v4.w;
+                }
+                return;
+            }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = cur.row0 + wm * 64 + i * 16 + (lane & 15);
@@ -474,76 +519,142 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
                 scol[j][v] = block_w ? 1.0f : (w_quant == MOE_W_PER_EXPERT ? sb[cur.e] : sb[(int64_t)cur.e * N + (n < N ? n : N - 1)]);
             }
 
+        };
+        if constexpr (FP4 || KDEP) load_scales();
+
         v4f acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        for (int k = 0; k < nk; ++k) {
-            if (k + 1 < nk) wait_vmcnt<kDmaN>();
-            else wait_vmcnt<0>();
-            if (group_act && tid < DBM) s_sa[k % kDStages][tid] = q;
-            __syncthreads();  // stage k complete; every wave is done with stage k-1
-            if (group_act && k + 1 < nk) q = sa[(int64_t)cur.sa_row * KB + k + 1];
-            // the FP8 path issues the DMA of step k+2 after this step's MFMAs (a
-            // wave whose loads stall in the address unit then has its matrix work
-            // queued already; 3-8 % faster), the other paths before its reads
-            if (FP4 || KDEP) { if (k + 2 < nk) issue(cur, k + 2); }
-
-            const uint8_t* la = lds + (k % kDStages) * kDStage;
-            const uint8_t* lb = la + kDStageA;
-            v8i af[4], bfr[4];
-            if (FP4) {
-                // lane l: 16 bytes = the 32 codes of K block l / 16 of row l % 16,
-                // and that block's E8M0 scale; the activations in the matching order
+        if constexpr (!FP4 && !KDEP) {
+            // operands of step k+1 are read into registers while step k's MFMAs run
+            v8i fa0[4], fb0[4], fa1[4], fb1[4];
+            auto read_step = [&](int k, v8i (&fa)[4], v8i (&fb)[4]) {
+                const uint8_t* la = lds + (k % kDStages) * kDStage;
+                const uint8_t* lb = la + kDStageA;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) af[i] = lds_operand_x4(la, wm * 64 + i * 16 + (lane & 15), lane);
-                const uint8_t* lsc = la + kDStageS4;
-                int scl[4];
+                for (int i = 0; i < 4; ++i) fa[i] = lds_operand(la, wm * 64 + i * 16 + (lane & 15), lane);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int rb = wn * 64 + j * 16 + (lane & 15);
-                    const uint4 q = *(const uint4*)(lb + rb * 64 + (fp4_pos(rb, lane >> 4) << 4));
-                    bfr[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-                    scl[j] = (int)lsc[rb * 4 + (lane >> 4)];
-                }
+                for (int j = 0; j < 4; ++j) fb[j] = lds_operand(lb, wn * 64 + j * 16 + (lane & 15), lane);
+            };
+            auto mfmas = [&](v8i (&ca)[4], v8i (&cb)[4]) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            bfr[j], af[i], acc[i][j], 4, 0, 0, scl[j], 0, 127);
+                            cb[j], ca[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+            };
+            // one of the wave's six DMA instructions of K step k (0-1: A, 2-5: B)
+            auto dma_one = [&](const DTile& t, int k, int i) {
+                const uint32_t st = lds0 + (uint32_t)((k % kDStages) * kDStage);
+                if (i < kDmaA) {
+                    dma16(uniform_ptr(t.a_g + k * DBK), t.a_off[i],
+                          __builtin_amdgcn_readfirstlane(st + (wid * kDmaA + i) * 1024));
+                } else {
+                    dma16(uniform_ptr(t.b_g + k * DBK), t.b_off[i - kDmaA],
+                          __builtin_amdgcn_readfirstlane(st + kDStageA + (wid * kDmaB + i - kDmaA) * 1024));
+                }
+            };
+            // step k (k + 1 < nk): publish step k+1; then eight groups of one operand
+            // read of step k+1, two MFMAs of step k and (groups 0-5) one DMA of step k+3
+            auto body = [&](int k, v8i (&ca)[4], v8i (&cb)[4], v8i (&na)[4], v8i (&nb)[4]) {
+                if (k + 2 < nk) wait_vmcnt<kDma>();
+                else wait_vmcnt<0>();
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of step k are done
+                __syncthreads();  // step k+1 complete in LDS; the slot of step k is free
+                const uint8_t* la1 = lds + ((k + 1) % kDStages) * kDStage;
+                const uint8_t* lb1 = la1 + kDStageA;
+                const bool more = k + 3 < nk;
+#pragma unroll
+                for (int g = 0; g < 8; ++g) {
+                    if (g < 4) na[g] = lds_operand(la1, wm * 64 + g * 16 + (lane & 15), lane);
+                    else nb[g - 4] = lds_operand(lb1, wn * 64 + (g - 4) * 16 + (lane & 15), lane);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int i = (2 * g + h) >> 2, j = (2 * g + h) & 3;
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            cb[j], ca[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (g < kDma && more) dma_one(cur, k + 3, g);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            if (nk > 1) wait_vmcnt<kDma>();
+            else wait_vmcnt<0>();
+            __syncthreads();  // step 0 complete
+            read_step(0, fa0, fb0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (nk > 2) issue(cur, 2);
+            int k = 0;
+            for (; k + 2 < nk; k += 2) {
+                body(k, fa0, fb0, fa1, fb1);
+                body(k + 1, fa1, fb1, fa0, fb0);
+            }
+            if (k + 1 < nk) {
+                body(k, fa0, fb0, fa1, fb1);
+                mfmas(fa1, fb1);
             } else {
+                mfmas(fa0, fb0);
+            }
+        } else {
+            for (int k = 0; k < nk; ++k) {
+                if (k + 1 < nk) wait_vmcnt<kDmaN>();
+                else wait_vmcnt<0>();
+                if (group_act && tid < DBM) s_sa[k % kDStages][tid] = q;
+                __syncthreads();  // stage k complete; every wave is done with stage k-1
+                if (group_act && k + 1 < nk) q = sa[(int64_t)cur.sa_row * KB + k + 1];
+                if (k + 2 < nk) issue(cur, k + 2);
+
+                const uint8_t* la = lds + (k % kDStages) * kDStage;
+                const uint8_t* lb = la + kDStageA;
+                v8i af[4], bfr[4];
+                if (FP4) {
+                    // lane l: 16 bytes = the 32 codes of K block l / 16 of row l % 16,
+                    // and that block's E8M0 scale; the activations in the matching order
 #pragma unroll
-                for (int i = 0; i < 4; ++i) af[i] = lds_operand(la, wm * 64 + i * 16 + (lane & 15), lane);
+                    for (int i = 0; i < 4; ++i) af[i] = lds_operand_x4(la, wm * 64 + i * 16 + (lane & 15), lane);
+                    const uint8_t* lsc = la + kDStageS4;
+                    int scl[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bfr[j] = lds_operand(lb, wn * 64 + j * 16 + (lane & 15), lane);
-                if (!KDEP) {
+                    for (int j = 0; j < 4; ++j) {
+                        const int rb = wn * 64 + j * 16 + (lane & 15);
+                        const uint4 q = *(const uint4*)(lb + rb * 64 + (fp4_pos(rb, lane >> 4) << 4));
+                        bfr[j] = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+                        scl[j] = (int)lsc[rb * 4 + (lane >> 4)];
+                    }
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                bfr[j], af[i], acc[i][j], 0, 0, 0, 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);  // keep the DMA after the MFMAs
-                    if (k + 2 < nk) issue(cur, k + 2);
+                                bfr[j], af[i], acc[i][j], 4, 0, 0, scl[j], 0, 127);
                 } else {
-                    const float sbv = block_w ? sb[((int64_t)cur.e * NB + cur.nb_w) * KB + k] : 1.0f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float f = (group_act ? s_sa[k % kDStages][wm * 64 + i * 16 + (lane & 15)] : 1.0f) * sbv;
+                    for (int i = 0; i < 4; ++i) af[i] = lds_operand(la, wm * 64 + i * 16 + (lane & 15), lane);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                bfr[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                    for (int j = 0; j < 4; ++j) bfr[j] = lds_operand(lb, wn * 64 + j * 16 + (lane & 15), lane);
+                    {  // K-dependent scales
+                        const float sbv = block_w ? sb[((int64_t)cur.e * NB + cur.nb_w) * KB + k] : 1.0f;
 #pragma unroll
-                            for (int v = 0; v < 4; ++v) acc[i][j][v] = acc[i][j][v] + t[v] * f;
+                        for (int i = 0; i < 4; ++i) {
+                            const float f = (group_act ? s_sa[k % kDStages][wm * 64 + i * 16 + (lane & 15)] : 1.0f) * sbv;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    bfr[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                                for (int v = 0; v < 4; ++v) acc[i][j][v] = acc[i][j][v] + t[v] * f;
+                            }
                         }
                     }
                 }
             }
         }
+        if constexpr (!FP4 && !KDEP) load_scales();
         __syncthreads();  // every wave is done with the operand stages
 
         // next tile: its first two stages (slots 0 and 1) load during this epilogue
@@ -553,6 +664,7 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
         if (has_next) {
             nxt = setup(lt_next);
             if (group_act) q = sa[(int64_t)nxt.sa_row * KB];
+            if constexpr (!FP4 && !KDEP) issue_scales(nxt, par ^ 1);
             issue(nxt, 0);
             if (nk > 1) issue(nxt, 1);
         }
@@ -590,6 +702,7 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
         if (!has_next) break;
         cur = nxt;
         lt = lt_next;
+        par ^= 1;
     }
 }
 
