@@ -377,7 +377,7 @@ def cpu_baseline(cfg, inp, sample_tokens):
     threads = len(os.sched_getaffinity(0))
     oracle.set_threads(threads)
     if not sample_tokens:
-        sample_tokens = {"tiny": 16, "dsv3_decode_ep": 128, "dsv3_prefill_ep": 1024,
+        sample_tokens = {"tiny": 16, "dsv3_decode_ep": 128, "dsv3_prefill_ep": 3072,
                          "mixtral": 64, "skewed_block": 512}.get(cfg.name, 256)
     Ts = min(sample_tokens, cfg.T)
     sub = dataclasses.replace(inp, cfg=dataclasses.replace(cfg, T=Ts), x=inp.x[:Ts],
