@@ -688,7 +688,10 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
                         make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
                 }
             }
-            __syncthreads();  // the staged half is complete (lanes read other lanes' values)
+            // the staging area is the wave's own: its LDS writes are complete
+            // (in order, one wave) before its lanes read each other's values
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int rl = t * 8 + (lane >> 3), qc = lane & 7;
@@ -697,7 +700,8 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
                 const uint4 v = *(const uint4*)(ep + ep_off(rl, qc));
                 if (r < cur.row_end && n < N) *(uint4*)(C + (int64_t)r * N + n) = v;
             }
-            __syncthreads();  // the half has been read back before the slot is reused
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // the half is read back before it is overwritten
+            __builtin_amdgcn_wave_barrier();
         }
         if (!has_next) break;
         cur = nxt;
