@@ -48,9 +48,7 @@ __device__ __forceinline__ void silu_mul16(const uint16_t* __restrict__ gu, int6
     for (int q = 0; q < 8; ++q) {
         const float g0 = bf16_lo(g[q]), g1 = bf16_hi(g[q]);
         const float u0 = bf16_lo(u[q]), u1 = bf16_hi(u[q]);
-        const float s0 = g0 / (1.0f + exp_fixed(-g0));
-        const float s1 = g1 / (1.0f + exp_fixed(-g1));
-        h[q] = f32_to_bf16_bits(s0 * u0) | (f32_to_bf16_bits(s1 * u1) << 16);
+        h[q] = bf16x2_rne(silu_fixed(g0) * u0, silu_fixed(g1) * u1);
     }
     h0 = make_uint4(h[0], h[1], h[2], h[3]);
     h1 = make_uint4(h[4], h[5], h[6], h[7]);
@@ -102,9 +100,7 @@ __device__ __forceinline__ void silu_mul16_from(const GU16& v, int I, int c, uin
     for (int q = 0; q < 8; ++q) {
         const float g0 = bf16_lo(g[q]), g1 = bf16_hi(g[q]);
         const float u0 = bf16_lo(u[q]), u1 = bf16_hi(u[q]);
-        const float s0 = g0 / (1.0f + exp_fixed(-g0));
-        const float s1 = g1 / (1.0f + exp_fixed(-g1));
-        h[q] = f32_to_bf16_bits(s0 * u0) | (f32_to_bf16_bits(s1 * u1) << 16);
+        h[q] = bf16x2_rne(silu_fixed(g0) * u0, silu_fixed(g1) * u1);
     }
     h0 = make_uint4(h[0], h[1], h[2], h[3]);
     h1 = make_uint4(h[4], h[5], h[6], h[7]);

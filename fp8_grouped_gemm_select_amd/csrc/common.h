@@ -55,13 +55,43 @@ __device__ __forceinline__ float exp_fixed(float x) {
     return __builtin_ldexpf(p, (int)n);
 }
 
-__device__ __forceinline__ float sigmoid_fixed(float x) { return 1.0f / (1.0f + exp_fixed(-x)); }
+// n / d for d in [1, 2^116] and finite n: the reciprocal-and-corrections
+// sequence of the compiler's IEEE division without its range scaling
+// (v_div_scale / v_div_fmas / v_div_fixup), and the sign of n copied onto the
+// result (the corrections turn -0 / d into +0). In that range the scaling is
+// the identity unless |n| < 2^-103, so the quotient is the correctly rounded
+// one; below, it may differ in the last place of a value under 2^-102 and
+// keeps the sign of n.
+__device__ __forceinline__ float div_by_ge1(float n, float d) {
+    float r = __builtin_amdgcn_rcpf(d);
+    const float e = __builtin_fmaf(-d, r, 1.0f);
+    r = __builtin_fmaf(e, r, r);
+    float q = n * r;
+    float rem = __builtin_fmaf(-d, q, n);
+    q = __builtin_fmaf(rem, r, q);
+    rem = __builtin_fmaf(-d, q, n);
+    return __builtin_copysignf(__builtin_fmaf(rem, r, q), n);
+}
+
+// 1 / (1 + exp(-x)): the denominator lies in [1, 1 + e^80], the numerator is 1.
+__device__ __forceinline__ float sigmoid_fixed(float x) { return div_by_ge1(1.0f, 1.0f + exp_fixed(-x)); }
+
+// x * sigmoid(x) as x / (1 + exp(-x)).
+__device__ __forceinline__ float silu_fixed(float x) { return div_by_ge1(x, 1.0f + exp_fixed(-x)); }
 
 // bf16 <-> fp32 (round to nearest even for finite values).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float v) {
     uint32_t u = __float_as_uint(v);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return u >> 16;
+}
+// Two fp32 values rounded to nearest even bf16 by one v_cvt_pk_bf16_f32, packed
+// (a in the low half); equal to f32_to_bf16_bits for finite values.
+typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float moe_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    const moe_f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, moe_bf16x2));
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -681,11 +681,11 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int cl = j * 16 + (lane >> 4) * 4;
-                    uint32_t hb[4];
+                    float hv[4];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) hb[v] = f32_to_bf16_bits(acc[i][j][v] * (srow[i] * scol[j][v]));
+                    for (int v = 0; v < 4; ++v) hv[v] = acc[i][j][v] * (srow[i] * scol[j][v]);
                     *(uint2*)(ep + ep_off(rl, cl >> 3) + (cl & 7) * 2) =
-                        make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                        make_uint2(bf16x2_rne(hv[0], hv[1]), bf16x2_rne(hv[2], hv[3]));
                 }
             }
             // the staging area is the wave's own: its LDS writes are complete
@@ -896,11 +896,11 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_fp4_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int cl = j * 16 + (lane >> 4) * 4;
-                    uint32_t hb[4];
+                    float hv[4];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) hb[v] = f32_to_bf16_bits(acc[i][j][v] * (srow[i] * scol[j][v]));
+                    for (int v = 0; v < 4; ++v) hv[v] = acc[i][j][v] * (srow[i] * scol[j][v]);
                     *(uint2*)(ep + ep_off(rl, cl >> 3) + (cl & 7) * 2) =
-                        make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                        make_uint2(bf16x2_rne(hv[0], hv[1]), bf16x2_rne(hv[2], hv[3]));
                 }
             }
             __syncthreads();

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void post_reorder8_kernel(const uint16_t* __re
         }
         uint32_t o[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = f32_to_bf16_bits(acc[2 * q]) | (f32_to_bf16_bits(acc[2 * q + 1]) << 16);
+        for (int q = 0; q < 8; ++q) o[q] = bf16x2_rne(acc[2 * q], acc[2 * q + 1]);
         uint4* po = (uint4*)(out + t * H + c);
         po[0] = make_uint4(o[0], o[1], o[2], o[3]);
         po[1] = make_uint4(o[4], o[5], o[6], o[7]);
@@ -110,10 +110,10 @@ __global__ __launch_bounds__(256) void post_reorder_kernel(const uint16_t* __res
             }
         }
         uint4 o;
-        o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
-        o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
-        o.z = f32_to_bf16_bits(acc[4]) | (f32_to_bf16_bits(acc[5]) << 16);
-        o.w = f32_to_bf16_bits(acc[6]) | (f32_to_bf16_bits(acc[7]) << 16);
+        o.x = bf16x2_rne(acc[0], acc[1]);
+        o.y = bf16x2_rne(acc[2], acc[3]);
+        o.z = bf16x2_rne(acc[4], acc[5]);
+        o.w = bf16x2_rne(acc[6], acc[7]);
         *(uint4*)(out + t * H + c) = o;
     }
 }

@@ -317,6 +317,59 @@ def test_act_requant_ragged(act_quant, dims):
     assert np.array_equal(a_s[:n].view(np.uint32), s_ref[:n].view(np.uint32))
 
 
+def _act_edge_rows(I=256, seed=5):
+    """gate / up rows with extreme values: signed zeros, bf16 subnormals, values
+    around 2^-103 (where the kernel's division skips its range scaling), huge
+    gates whose exp(-g) clamps, and rows whose amax falls below the 1e-10 floor."""
+    g = np.random.default_rng(seed)
+    special = np.array([0.0, -0.0, 1e-38, -1e-38, 2.0 ** -103, -(2.0 ** -103), 2.0 ** -102, -(2.0 ** -104),
+                        1e-35, -1e-35, 1e-20, -1e-20, 80.0, -80.0, 80.5, -80.5, 100.0, -100.0, 1e4, -1e4,
+                        1e30, -1e30, 1e35, -1e35, 0.5, -0.5, 3.0, -3.0], dtype=np.float64)
+    rows_g, rows_u = [], []
+    for r in range(8):
+        gate = g.standard_normal(2 * I // 2) * 2.0
+        up = g.standard_normal(2 * I // 2)
+        pos = g.permutation(I)[:len(special)]
+        gate[pos] = special
+        if r == 1:
+            up[pos[:6]] = [0.0, -0.0, 1e-30, -1e-30, 1e-38, -1e-38]
+        if r == 2:      # the whole row tiny: scale floored, every code a signed zero
+            gate *= 1e-31
+        if r == 3:      # gate all -0 / +0
+            gate = np.where(np.arange(I) % 2 == 0, -0.0, 0.0)
+        if r == 4:      # huge gates, tiny ups: finite products
+            gate = np.sign(gate) * 1e30
+            up = up * 1e-9
+        if r == 5:      # negative gates beyond the exp clamp
+            gate = -np.abs(gate) * 60.0
+        rows_g.append(gate)
+        rows_u.append(up)
+    gate = np.array(rows_g, dtype=np.float32)
+    up = np.array(rows_u, dtype=np.float32)
+    gb = W.to_bf16_bits(gate)
+    ub = W.to_bf16_bits(up)
+    gb[0, :4] = [0x0001, 0x8001, 0x007F, 0x807F]       # bf16 subnormals
+    gb[0, 4:6] = [0x8000, 0x0000]
+    return np.concatenate([gb, ub], axis=1)
+
+
+@pytest.mark.parametrize("act_quant", [W.ACT_PER_TENSOR, W.ACT_PER_TOKEN, W.ACT_PER_GROUP])
+def test_act_requant_extreme_values(act_quant):
+    """SiLU division, bf16 rounding and FP8 encoding at extreme magnitudes: codes
+    and scales bit-exact against the oracle."""
+    gu = _act_edge_rows()
+    M = gu.shape[0]
+    seg = np.array([0, 3, M], dtype=np.int32)
+    I = gu.shape[1] // 2
+    print(f"act_requant extreme values M={M} I={I} mode={act_quant}", flush=True)
+    a_ref, s_ref = oracle.act_requant(gu, seg, act_quant)
+    a_q, a_s = G.run_act(gu, seg, act_quant)
+    assert np.array_equal(a_q[:M], a_ref[:M])
+    Gq = 1 if act_quant == W.ACT_PER_TOKEN else -(-I // 128)
+    n = 1 if act_quant == W.ACT_PER_TENSOR else M * Gq
+    assert np.array_equal(a_s[:n].view(np.uint32), s_ref[:n].view(np.uint32))
+
+
 @pytest.mark.parametrize("name", ["dsv3_prefill_ep", "mixtral", "skewed_block"])
 def test_act_requant_full_size(name):
     cfg, inp, ids, _ = routed(name)
