@@ -11,9 +11,61 @@
 namespace moe {
 namespace {
 
-// topk <= 8: each lane covers 16 columns (32 bytes) per iteration; the loads of
-// every local slot of an iteration are issued together, then accumulated in
-// slot order (the same fp32 order as the general kernel below).
+// topk <= 8: the token's local slots are compacted in slot order (n of them,
+// wave-uniform); each lane covers 16 columns (32 bytes) per iteration and the
+// loads of U iterations of all n slots are issued together, then accumulated
+// in slot order (the same fp32 order as the general kernel below). Fewer local
+// slots leave room for more iterations in flight: U = 4 for n <= 2, 2 for
+// n <= 4, else 1.
+template <int S, int U>
+__device__ __forceinline__ void combine_token(const uint16_t* __restrict__ down, const int (&rows)[S],
+                                              const float (&wj)[S], int n, int H, int lane,
+                                              uint16_t* __restrict__ orow) {
+    for (int c0 = lane * 16; c0 < H; c0 += 1024 * U) {
+        uint4 v[S][U][2];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            if (s < n) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * 1024;
+                    if (c < H) {
+                        const uint4* p = (const uint4*)(down + (int64_t)rows[s] * H + c);
+                        v[s][u][0] = p[0];
+                        v[s][u][1] = p[1];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * 1024;
+            if (c >= H) break;
+            float acc[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                if (s < n) {
+                    const uint32_t d[8] = {v[s][u][0].x, v[s][u][0].y, v[s][u][0].z, v[s][u][0].w,
+                                           v[s][u][1].x, v[s][u][1].y, v[s][u][1].z, v[s][u][1].w};
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        acc[2 * q] = acc[2 * q] + wj[s] * bf16_lo(d[q]);
+                        acc[2 * q + 1] = acc[2 * q + 1] + wj[s] * bf16_hi(d[q]);
+                    }
+                }
+            }
+            uint32_t o[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) o[q] = bf16x2_rne(acc[2 * q], acc[2 * q + 1]);
+            uint4* po = (uint4*)(orow + c);
+            po[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            po[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void post_reorder8_kernel(const uint16_t* __restrict__ down,
                                                             const int32_t* __restrict__ src2dst,
                                                             const float* __restrict__ w, int64_t T,
@@ -32,45 +84,29 @@ __global__ __launch_bounds__(256) void post_reorder8_kernel(const uint16_t* __re
             wt = w[t * topk + lane];
         }
     }
-    const uint64_t mask = __ballot(r >= 0);
+    // local slots in ascending slot order: rows[q], wj[q] for q < n
+    uint64_t m = __ballot(r >= 0);
+    const int n = __builtin_popcountll(m);
     int rows[K8];
     float wj[K8];
 #pragma unroll
-    for (int j = 0; j < K8; ++j) {
-        rows[j] = __builtin_amdgcn_readlane(r, j);
-        wj[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), j));
+    for (int q = 0; q < K8; ++q) {
+        const int j = m ? __builtin_ctzll(m) : 0;
+        m &= m - 1;
+        rows[q] = __builtin_amdgcn_readlane(r, j);
+        wj[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), j));
     }
-    for (int c = lane * 16; c < H; c += 1024) {
-        uint4 v[K8][2];
-#pragma unroll
-        for (int j = 0; j < K8; ++j) {
-            if ((mask >> j) & 1ull) {
-                const uint4* p = (const uint4*)(down + (int64_t)rows[j] * H + c);
-                v[j][0] = p[0];
-                v[j][1] = p[1];
-            }
-        }
-        float acc[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[q] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < K8; ++j) {
-            if ((mask >> j) & 1ull) {
-                const uint32_t d[8] = {v[j][0].x, v[j][0].y, v[j][0].z, v[j][0].w,
-                                       v[j][1].x, v[j][1].y, v[j][1].z, v[j][1].w};
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    acc[2 * q] = acc[2 * q] + wj[j] * bf16_lo(d[q]);
-                    acc[2 * q + 1] = acc[2 * q + 1] + wj[j] * bf16_hi(d[q]);
-                }
-            }
-        }
-        uint32_t o[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = bf16x2_rne(acc[2 * q], acc[2 * q + 1]);
-        uint4* po = (uint4*)(out + t * H + c);
-        po[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        po[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    uint16_t* orow = out + t * H;
+    if (n <= 2) {
+        const int r2[2] = {rows[0], rows[1]};
+        const float w2[2] = {wj[0], wj[1]};
+        combine_token<2, 4>(down, r2, w2, n, H, lane, orow);
+    } else if (n <= 4) {
+        const int r4[4] = {rows[0], rows[1], rows[2], rows[3]};
+        const float w4[4] = {wj[0], wj[1], wj[2], wj[3]};
+        combine_token<4, 2>(down, r4, w4, n, H, lane, orow);
+    } else {
+        combine_token<K8, 1>(down, rows, wj, n, H, lane, orow);
     }
 }
 

@@ -1,5 +1,6 @@
 // Stage 1: the fused gate (scoring, grouped top-k, renormalisation, routed
-// scaling factor), one wavefront per token.
+// scaling factor): sixteen lanes per token where the expert count allows it,
+// else one wavefront per token.
 //
 // Follows "[1/2] sgl-kernel: Fuse routed scaling factor into select_experts"
 // (sglang PR #8364), Motivation and Modifications: the scaling factor is
@@ -208,6 +209,137 @@ __global__ __launch_bounds__(256) void select_experts_kernel(
     }
 }
 
+// Sixteen lanes per token, four tokens per wave (E = 16 * EPL, EPL in {4, 8, 16}):
+// the serial part of the selection (one round per chosen expert) runs once for
+// four tokens, and every cross-lane step stays inside a 16-lane DPP row.
+// Lane rl = lane % 16 of row lane / 16 owns experts rl * EPL + i. Same
+// per-expert arithmetic and ordering rules as select_experts_kernel; a group
+// spans LPG = (E / n_group) / EPL lanes (1, 2, 4, 8 or 16) when n_group > 1.
+template <int EPL>
+__global__ __launch_bounds__(256) void select_rows_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int topk,
+    int n_group, int topk_group, int score_fn, int renormalize, float rsf, int apply_rsf,
+    int n_shared, float shared_weight, int stride, int32_t* __restrict__ ids_out,
+    float* __restrict__ w_out) {
+    constexpr int E = 16 * EPL;
+    const int lane = threadIdx.x & 63, rl = lane & 15, rbase = lane & 48;
+    const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const bool active = t < T;
+    const float* l = logits + (active ? t : 0) * E + rl * EPL;
+
+    float lraw[EPL], braw[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; i += 4) {
+        const float4 v = *(const float4*)(l + i);
+        lraw[i] = v.x; lraw[i + 1] = v.y; lraw[i + 2] = v.z; lraw[i + 3] = v.w;
+        if (bias) {
+            const float4 b = *(const float4*)(bias + rl * EPL + i);
+            braw[i] = b.x; braw[i + 1] = b.y; braw[i + 2] = b.z; braw[i + 3] = b.w;
+        } else {
+            braw[i] = braw[i + 1] = braw[i + 2] = braw[i + 3] = 0.0f;
+        }
+    }
+    float key[EPL], sc[EPL];
+    bool ok[EPL];
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        ok[i] = active;
+        const float lv = active ? lraw[i] : 0.0f;
+        if (score_fn == MOE_SCORE_SIGMOID) {
+            sc[i] = sigmoid_fixed(lv);
+            key[i] = bias ? sc[i] + braw[i] : sc[i];
+        } else {
+            sc[i] = lv;
+            key[i] = lv;
+            lmax = fmaxf(lmax, lv);
+        }
+    }
+
+    if (n_group > 1) {
+        const int lpg = (E / n_group) / EPL;
+        float t1 = -INFINITY, t2 = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) top2_merge(t1, t2, key[i], -INFINITY);
+        if (lpg >= 2) top2_step<kDppXor1>(t1, t2);
+        if (lpg >= 4) top2_step<kDppXor2>(t1, t2);
+        if (lpg >= 8) top2_step<kDppHalfMirror>(t1, t2);
+        if (lpg >= 16) top2_step<kDppMirror>(t1, t2);
+        const float gscore = t1 + t2;  // a group holds at least EPL >= 4 experts
+        const int g = rl / lpg;
+        int rank = 0;
+        for (int g2 = 0; g2 < n_group; ++g2) {
+            const float o = __shfl(gscore, rbase + g2 * lpg, MOE_WAVE);
+            rank += (o > gscore || (o == gscore && g2 < g)) ? 1 : 0;
+        }
+        const bool keep = rank < topk_group;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) ok[i] = ok[i] && keep;
+    }
+
+    // round j: the row's best allowed key (larger key, then lower expert id)
+    int my_id = 0;
+    float my_sc = 0.0f;
+    for (int j = 0; j < topk; ++j) {
+        float lb = -INFINITY, lsc = 0.0f;
+        int li = -1;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (ok[i] && (li < 0 || key[i] > lb)) { lb = key[i]; li = i; lsc = sc[i]; }
+        float m = li >= 0 ? lb : -INFINITY;
+        m = fmaxf(m, dpp<kDppXor1>(m));
+        m = fmaxf(m, dpp<kDppXor2>(m));
+        m = fmaxf(m, dpp<kDppHalfMirror>(m));
+        m = fmaxf(m, dpp<kDppMirror>(m));
+        const uint64_t owners = __ballot(li >= 0 && lb == m);
+        const uint32_t sub = (uint32_t)(owners >> rbase) & 0xFFFFu;
+        const int owner = sub ? __builtin_ctz(sub) : 0;
+        const int wi = __shfl(li, rbase + owner, MOE_WAVE);
+        const float wsc = __shfl(lsc, rbase + owner, MOE_WAVE);
+        if (sub && rl == j) { my_id = owner * EPL + wi; my_sc = wsc; }
+        const bool mine = sub && rl == owner;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) ok[i] = ok[i] && !(mine && i == wi);
+    }
+
+    float v = 0.0f, all = 1.0f;
+    if (score_fn == MOE_SCORE_SOFTMAX) {
+        float m = lmax;
+        m = fmaxf(m, dpp<kDppXor1>(m));
+        m = fmaxf(m, dpp<kDppXor2>(m));
+        m = fmaxf(m, dpp<kDppHalfMirror>(m));
+        m = fmaxf(m, dpp<kDppMirror>(m));
+        if (rl < topk) v = exp_fixed(my_sc - m);
+        if (!renormalize) {
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (active) part += exp_fixed(sc[i] - m);
+            part += dpp<kDppXor1>(part);
+            part += dpp<kDppXor2>(part);
+            part += dpp<kDppHalfMirror>(part);
+            part += dpp<kDppMirror>(part);
+            all = part;
+        }
+    } else if (rl < topk) {
+        v = my_sc;
+    }
+    float sel = rl < topk ? v : 0.0f;
+    sel += dpp<kDppXor1>(sel);
+    sel += dpp<kDppXor2>(sel);
+    sel += dpp<kDppHalfMirror>(sel);
+    sel += dpp<kDppMirror>(sel);
+    float w = v / (renormalize ? sel : all);
+    if (apply_rsf) w = w * rsf;
+    if (active && rl < topk) {
+        ids_out[t * stride + rl] = my_id;
+        w_out[t * stride + rl] = w;
+    } else if (active && rl < topk + n_shared) {
+        ids_out[t * stride + rl] = E + (rl - topk);
+        w_out[t * stride + rl] = shared_weight;
+    }
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -232,6 +364,25 @@ int launch_select_experts(const float* logits, const float* correction_bias, int
     if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_weights))
         return MOE_ERR_INVALID_ARG;
     (void)hipGetLastError();
+    // sixteen lanes per token when E = 16 * EPL (EPL 4, 8 or 16), every output
+    // slot fits a lane of the row, and a group covers whole lanes
+    const int epl16 = E % 16 == 0 ? E / 16 : 0;
+    const int gsz = E / n_group;
+    const bool rows_ok = (epl16 == 4 || epl16 == 8 || epl16 == 16) && topk + n_shared <= 16 &&
+                         (!correction_bias || aligned16(correction_bias)) &&
+                         (n_group == 1 || (gsz % epl16 == 0 && 16 % (gsz / epl16) == 0));
+    if (rows_ok) {
+        const dim3 g16((unsigned)ceil_div(T, 16)), b16(256);
+#define MOE_LAUNCH_ROWS(EPL)                                                                      \
+    hipLaunchKernelGGL(select_rows_kernel<EPL>, g16, b16, 0, s, logits, correction_bias, T, topk,  \
+                       n_group, topk_group, score_fn, renormalize, routed_scaling_factor,        \
+                       apply_rsf, n_shared, shared_weight, topk + n_shared, topk_ids, topk_weights)
+        if (epl16 == 4) MOE_LAUNCH_ROWS(4);
+        else if (epl16 == 8) MOE_LAUNCH_ROWS(8);
+        else MOE_LAUNCH_ROWS(16);
+#undef MOE_LAUNCH_ROWS
+        return launch_status();
+    }
     const dim3 grid((unsigned)ceil_div(T, kTokensPerBlock)), block(256);
 #define MOE_LAUNCH_SELECT(EPL)                                                                     \
     hipLaunchKernelGGL(select_experts_kernel<EPL>, grid, block, 0, s, logits, correction_bias, T, \

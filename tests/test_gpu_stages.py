@@ -90,6 +90,55 @@ def test_select_experts_edges(case):
     check_weights(w, w_ref)
 
 
+@pytest.mark.parametrize("case", [
+    # (E, topk, n_group, topk_group, score_fn, T): sixteen lanes per token, a group
+    # spanning 1, 2, 4, 8 or 16 lanes, up to 16 output slots, partial blocks
+    (256, 8, 16, 8, W.SCORE_SIGMOID, 33),
+    (256, 8, 8, 4, W.SCORE_SIGMOID, 17),
+    (128, 6, 4, 2, W.SCORE_SIGMOID, 40),
+    (256, 16, 2, 1, W.SCORE_SIGMOID, 21),
+    (64, 16, 1, 1, W.SCORE_SIGMOID, 19),
+    (64, 16, 1, 1, W.SCORE_SOFTMAX, 50),
+    (128, 1, 1, 1, W.SCORE_SOFTMAX, 3),
+    (256, 12, 1, 1, W.SCORE_SOFTMAX, 16),
+])
+def test_select_experts_row_layout(case):
+    E, topk, n_group, topk_group, score_fn, T = case
+    g = np.random.default_rng(E * 31 + topk)
+    logits = (g.standard_normal((T, E)) * 1.5).astype(np.float32)
+    logits[::5, :: 3] = np.round(logits[::5, ::3])  # some exact ties
+    bias = (g.standard_normal(E) * 0.01).astype(np.float32) if score_fn == W.SCORE_SIGMOID else None
+    kw = dict(topk=topk, n_group=n_group, topk_group=topk_group, score_fn=score_fn, renormalize=1,
+              rsf=2.5, apply_rsf=1)
+    print(f"select_experts row layout {case}", flush=True)
+    ids_ref, w_ref = oracle.select_experts(logits, bias, topk, n_group, topk_group, score_fn, 1, 2.5, 1)
+    ids, w = G.run_select(logits, bias, **kw)
+    assert np.array_equal(ids, ids_ref)
+    check_weights(w, w_ref)
+
+
+def test_select_experts_unaligned_bias():
+    """A correction bias that is not 16-byte aligned takes the one-wave-per-token
+    kernel; results are the same."""
+    g = np.random.default_rng(3)
+    T, E = 24, 256
+    logits = (g.standard_normal((T, E)) * 1.5).astype(np.float32)
+    bias = (g.standard_normal(E) * 0.01).astype(np.float32)
+    ids_ref, w_ref = oracle.select_experts(logits, bias, 8, 8, 4, W.SCORE_SIGMOID, 1, 2.5, 1)
+    store = G.up(np.concatenate([[0.0], bias]).astype(np.float32))
+    bt = store[1:]
+    ids = G.Guarded((T, 8), torch.int32)
+    w = G.Guarded((T, 8), torch.float32)
+    G.moe.moe_select_experts(G.up(logits), bt, ids.t, w.t, topk=8, n_group=8, topk_group=4,
+                             score_fn=W.SCORE_SIGMOID, renormalize=1, routed_scaling_factor=2.5,
+                             apply_rsf=1)
+    torch.cuda.synchronize()
+    ids.check("topk_ids")
+    w.check("topk_weights")
+    assert np.array_equal(ids.t.cpu().numpy(), ids_ref)
+    check_weights(w.t.cpu().numpy(), w_ref)
+
+
 # ---- stage 2 ----------------------------------------------------------------------
 
 def check_pre(res, ref_perm, ref_q, act_quant, H):
