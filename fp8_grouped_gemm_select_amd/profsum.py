@@ -53,7 +53,7 @@ def short_name(kernel: str) -> str:
 
 def stage_of(kernel: str):
     k = short_name(kernel)
-    if k.startswith("select_experts"):
+    if k.startswith("select_experts") or k.startswith("select_rows"):
         return "select"
     if k.startswith("pr_"):
         return "pre_reorder"
@@ -114,6 +114,16 @@ def trace_md(path, workload, command):
             v = _per_pass_sums(ds, st)
         if v:
             lines.append(f"| {st} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
+def stats_md(path):
+    """The profiler's own per-kernel summary (`--stats`), names shortened."""
+    lines = ["", "rocprofv3 `--stats` kernel summary of the same run:", "",
+             "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    for r in _rows(path):
+        lines.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
     return "\n".join(lines) + "\n"
 
 
@@ -200,6 +210,7 @@ def main(argv=None):
     a.add_argument("--workload", required=True)
     a.add_argument("--command", required=True)
     a.add_argument("--out", required=True)
+    a.add_argument("--stats", help="the run's --stats kernel summary CSV, appended as a table")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -212,6 +223,8 @@ def main(argv=None):
     if args.cmd == "trace":
         with open(args.out, "w") as f:
             f.write(trace_md(args.csv, args.workload, args.command))
+            if args.stats:
+                f.write(stats_md(args.stats))
     else:
         t = traffic(args.fetch_csv, args.write_csv, args.calib_bytes, args.workload, args.command)
         with open(args.out_json, "w") as f:

@@ -34,6 +34,7 @@ def test_short_names_and_stages():
     assert [profsum.stage_of(k) for k in KERNELS] == ["select", "pre_reorder", "pre_reorder", "gemm",
                                                       "act_requant", "gemm", "post_reorder"]
     assert profsum.stage_of("__amd_rocclr_copyBuffer") is None
+    assert profsum.stage_of("void moe::(anonymous namespace)::select_rows_kernel<16>(float const*)") == "select"
 
 
 def test_traffic_calibration_and_split(tmp_path):
