@@ -215,46 +215,49 @@ __global__ __launch_bounds__(256) void select_experts_kernel(
 // Lane rl = lane % 16 of row lane / 16 owns experts rl * EPL + i. Same
 // per-expert arithmetic and ordering rules as select_experts_kernel; a group
 // spans LPG = (E / n_group) / EPL lanes (1, 2, 4, 8 or 16) when n_group > 1.
-template <int EPL>
+template <int EPL, int SCORE>
 __global__ __launch_bounds__(256) void select_rows_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int topk,
-    int n_group, int topk_group, int score_fn, int renormalize, float rsf, int apply_rsf,
+    int n_group, int topk_group, int renormalize, float rsf, int apply_rsf,
     int n_shared, float shared_weight, int stride, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out) {
     constexpr int E = 16 * EPL;
+    static_assert(EPL <= 16, "the allowed set is a 16-bit mask per lane");
     const int lane = threadIdx.x & 63, rl = lane & 15, rbase = lane & 48;
     const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
     const bool active = t < T;
     const float* l = logits + (active ? t : 0) * E + rl * EPL;
+    // the bias loads go to the logits row when there is no bias (masked below),
+    // so every load of the lane is issued before the first use
+    const bool has_bias = SCORE == MOE_SCORE_SIGMOID && bias != nullptr;
+    const float* bl = has_bias ? bias + rl * EPL : l;
 
     float lraw[EPL], braw[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; i += 4) {
         const float4 v = *(const float4*)(l + i);
         lraw[i] = v.x; lraw[i + 1] = v.y; lraw[i + 2] = v.z; lraw[i + 3] = v.w;
-        if (bias) {
-            const float4 b = *(const float4*)(bias + rl * EPL + i);
+        if (SCORE == MOE_SCORE_SIGMOID) {
+            const float4 b = *(const float4*)(bl + i);
             braw[i] = b.x; braw[i + 1] = b.y; braw[i + 2] = b.z; braw[i + 3] = b.w;
-        } else {
-            braw[i] = braw[i + 1] = braw[i + 2] = braw[i + 3] = 0.0f;
         }
     }
     float key[EPL], sc[EPL];
-    bool ok[EPL];
     float lmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-        ok[i] = active;
         const float lv = active ? lraw[i] : 0.0f;
-        if (score_fn == MOE_SCORE_SIGMOID) {
+        if (SCORE == MOE_SCORE_SIGMOID) {
             sc[i] = sigmoid_fixed(lv);
-            key[i] = bias ? sc[i] + braw[i] : sc[i];
+            key[i] = has_bias ? sc[i] + braw[i] : sc[i];
         } else {
             sc[i] = lv;
             key[i] = lv;
             lmax = fmaxf(lmax, lv);
         }
     }
+    // bit i of okm: expert rl * EPL + i may still be chosen
+    uint32_t okm = active ? (EPL == 32 ? 0xFFFFFFFFu : ((1u << EPL) - 1u)) : 0u;
 
     if (n_group > 1) {
         const int lpg = (E / n_group) / EPL;
@@ -272,9 +275,7 @@ __global__ __launch_bounds__(256) void select_rows_kernel(
             const float o = __shfl(gscore, rbase + g2 * lpg, MOE_WAVE);
             rank += (o > gscore || (o == gscore && g2 < g)) ? 1 : 0;
         }
-        const bool keep = rank < topk_group;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) ok[i] = ok[i] && keep;
+        if (rank >= topk_group) okm = 0u;
     }
 
     // round j: the row's best allowed key (larger key, then lower expert id)
@@ -284,8 +285,12 @@ __global__ __launch_bounds__(256) void select_rows_kernel(
         float lb = -INFINITY, lsc = 0.0f;
         int li = -1;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (ok[i] && (li < 0 || key[i] > lb)) { lb = key[i]; li = i; lsc = sc[i]; }
+        for (int i = 0; i < EPL; ++i) {
+            const bool take = ((okm >> i) & 1u) && (li < 0 || key[i] > lb);
+            lb = take ? key[i] : lb;
+            lsc = take ? sc[i] : lsc;
+            li = take ? i : li;
+        }
         float m = li >= 0 ? lb : -INFINITY;
         m = fmaxf(m, dpp<kDppXor1>(m));
         m = fmaxf(m, dpp<kDppXor2>(m));
@@ -296,14 +301,14 @@ __global__ __launch_bounds__(256) void select_rows_kernel(
         const int owner = sub ? __builtin_ctz(sub) : 0;
         const int wi = __shfl(li, rbase + owner, MOE_WAVE);
         const float wsc = __shfl(lsc, rbase + owner, MOE_WAVE);
-        if (sub && rl == j) { my_id = owner * EPL + wi; my_sc = wsc; }
-        const bool mine = sub && rl == owner;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) ok[i] = ok[i] && !(mine && i == wi);
+        const bool hit = sub != 0;
+        my_id = (hit && rl == j) ? owner * EPL + wi : my_id;
+        my_sc = (hit && rl == j) ? wsc : my_sc;
+        okm &= (hit && rl == owner) ? ~(1u << wi) : 0xFFFFFFFFu;
     }
 
     float v = 0.0f, all = 1.0f;
-    if (score_fn == MOE_SCORE_SOFTMAX) {
+    if (SCORE == MOE_SCORE_SOFTMAX) {
         float m = lmax;
         m = fmaxf(m, dpp<kDppXor1>(m));
         m = fmaxf(m, dpp<kDppXor2>(m));
@@ -373,13 +378,19 @@ int launch_select_experts(const float* logits, const float* correction_bias, int
                          (n_group == 1 || (gsz % epl16 == 0 && 16 % (gsz / epl16) == 0));
     if (rows_ok) {
         const dim3 g16((unsigned)ceil_div(T, 16)), b16(256);
-#define MOE_LAUNCH_ROWS(EPL)                                                                      \
-    hipLaunchKernelGGL(select_rows_kernel<EPL>, g16, b16, 0, s, logits, correction_bias, T, topk,  \
-                       n_group, topk_group, score_fn, renormalize, routed_scaling_factor,        \
-                       apply_rsf, n_shared, shared_weight, topk + n_shared, topk_ids, topk_weights)
-        if (epl16 == 4) MOE_LAUNCH_ROWS(4);
-        else if (epl16 == 8) MOE_LAUNCH_ROWS(8);
-        else MOE_LAUNCH_ROWS(16);
+#define MOE_LAUNCH_ROWS(EPL, SC)                                                                  \
+    hipLaunchKernelGGL((select_rows_kernel<EPL, SC>), g16, b16, 0, s, logits, correction_bias, T, topk, \
+                       n_group, topk_group, renormalize, routed_scaling_factor, apply_rsf,       \
+                       n_shared, shared_weight, topk + n_shared, topk_ids, topk_weights)
+        if (score_fn == MOE_SCORE_SIGMOID) {
+            if (epl16 == 4) MOE_LAUNCH_ROWS(4, MOE_SCORE_SIGMOID);
+            else if (epl16 == 8) MOE_LAUNCH_ROWS(8, MOE_SCORE_SIGMOID);
+            else MOE_LAUNCH_ROWS(16, MOE_SCORE_SIGMOID);
+        } else {
+            if (epl16 == 4) MOE_LAUNCH_ROWS(4, MOE_SCORE_SOFTMAX);
+            else if (epl16 == 8) MOE_LAUNCH_ROWS(8, MOE_SCORE_SOFTMAX);
+            else MOE_LAUNCH_ROWS(16, MOE_SCORE_SOFTMAX);
+        }
 #undef MOE_LAUNCH_ROWS
         return launch_status();
     }
