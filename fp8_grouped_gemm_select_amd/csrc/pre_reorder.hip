@@ -250,33 +250,23 @@ __device__ __forceinline__ void scatter_token(
     const int G = (H + MOE_QB - 1) / MOE_QB;
     const int nit = (H + 1023) / 1024;  // iterations of 1024 columns (16 per lane)
     const uint4* xr = x + (t * H) / 8;   // 8 bf16 per uint4
+    // Columns past H read column 0 (a valid address) and are masked to zero with
+    // an AND, not a branch: a branch around the loads makes the compiler wait
+    // for each load before issuing the next.
     auto load16 = [&](int it, uint4& a, uint4& b) {
         const int c = it * 1024 + lane * 16;
-        if (c < H) {
-            a = xr[c / 8];
-            b = xr[c / 8 + 1];
-        } else {
-            a = make_uint4(0, 0, 0, 0);
-            b = a;
-        }
+        const int cc = c < H ? c : 0;
+        const uint32_t m = c < H ? 0xFFFFFFFFu : 0u;
+        const uint4 a0 = xr[cc / 8], b0 = xr[cc / 8 + 1];
+        a = make_uint4(a0.x & m, a0.y & m, a0.z & m, a0.w & m);
+        b = make_uint4(b0.x & m, b0.y & m, b0.z & m, b0.w & m);
     };
 
-    // per-token mode: the whole row goes to registers now, in flight while the
-    // destination rows are looked up
+    // the row's first kRegIters iterations go to registers now (every mode), in
+    // flight while the destination rows are looked up
     uint4 buf[kRegIters][2];
 #pragma unroll
-    for (int it = 0; it < kRegIters; ++it) buf[it][0] = buf[it][1] = make_uint4(0, 0, 0, 0);
-    if (MODE == MOE_ACT_PER_TOKEN) {
-#pragma unroll
-        for (int it = 0; it < kRegIters; ++it) {
-            const int c = it * 1024 + lane * 16;
-            const int cc = c < H ? c : 0;
-            const uint4 a0 = xr[cc / 8], b0 = xr[cc / 8 + 1];
-            const bool in = c < H;
-            buf[it][0] = in ? a0 : make_uint4(0, 0, 0, 0);
-            buf[it][1] = in ? b0 : make_uint4(0, 0, 0, 0);
-        }
-    }
+    for (int it = 0; it < kRegIters; ++it) load16(it, buf[it][0], buf[it][1]);
 
     int m_all = 0;
     const int base = expert_base(tot, num_local, e, lane, m_all);
@@ -302,7 +292,23 @@ __device__ __forceinline__ void scatter_token(
     };
 
     if (MODE == MOE_ACT_PER_GROUP) {
-        for (int it = 0; it < nit; ++it) {
+#pragma unroll
+        for (int it = 0; it < kRegIters; ++it) {
+            if (it >= nit) break;
+            const uint4 a = buf[it][0], b = buf[it][1];
+            const float gm = group8_max(amax16(a, b));
+            float s, inv;
+            dyn_scale(gm, s, inv);
+            store_rows(it, quant16(a, b, inv));
+            const int g = it * 8 + (lane >> 3);
+            for (int j = 0; j < topk; ++j) {
+                if ((local_mask >> j) & 1ull) {
+                    const int r = __builtin_amdgcn_readlane(dst, j);
+                    if ((lane & 7) == 0 && g < G) a_scale[(int64_t)r * G + g] = s;
+                }
+            }
+        }
+        for (int it = kRegIters; it < nit; ++it) {
             uint4 a, b;
             load16(it, a, b);
             const float gm = group8_max(amax16(a, b));
@@ -324,7 +330,10 @@ __device__ __forceinline__ void scatter_token(
     if (MODE == MOE_ACT_PER_TENSOR) {
         s = tscale[0];
         inv = tscale[1];
-        for (int it = 0; it < nit; ++it) {
+#pragma unroll
+        for (int it = 0; it < kRegIters; ++it)
+            if (it < nit) store_rows(it, quant16(buf[it][0], buf[it][1], inv));
+        for (int it = kRegIters; it < nit; ++it) {
             uint4 a, b;
             load16(it, a, b);
             store_rows(it, quant16(a, b, inv));
