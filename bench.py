@@ -53,10 +53,13 @@ def parse():
     return p.parse_args()
 
 
-def algorithmic_work(cfg, seg, a_scale_bytes13, a_scale_bytes2, w13_scale_numel, w2_scale_numel):
+def algorithmic_work(cfg, seg, a_scale_bytes13, a_scale_bytes2, w13_scale_numel, w2_scale_numel,
+                     tokens_local=None):
     """Bytes each stage must move (inputs read once, outputs written once) and GEMM FLOPs.
     Weights of experts with rows: e4m3 codes (1 byte each) or MXFP4 (half a byte
-    each plus one E8M0 byte per 32), and their fp32 scales."""
+    each plus one E8M0 byte per 32), and their fp32 scales. Stage 2 reads the x
+    rows of the `tokens_local` tokens that have a local pair (all T when not
+    given), plus all of x once more for the per-tensor amax."""
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.slots
     M = int(seg[-1])
     counts = np.diff(seg)
@@ -65,12 +68,12 @@ def algorithmic_work(cfg, seg, a_scale_bytes13, a_scale_bytes2, w13_scale_numel,
     per_w = (0.5 + 1.0 / 32) if cfg.w_fp4 else 1.0
     b13 = int(nonempty * 2 * I * H * per_w) + w13_scale_numel * 4 * nonempty // max(El, 1)
     b2 = int(nonempty * H * I * per_w) + w2_scale_numel * 4 * nonempty // max(El, 1)
-    tok_local = None
+    tok_local = T if tokens_local is None else int(tokens_local)
     work = {}
     work["select"] = dict(bytes=T * E * 4 + (E * 4 if cfg.use_bias else 0) + T * k * 8, flops=0)
     # pre_reorder: ids + x rows of tokens with a local pair (+ a second read of x for the
     # per-tensor amax), codes + scales of M rows, src2dst / dst2src / seg
-    work["pre_reorder"] = dict(bytes=T * k * 4 + T * H * 2 * (2 if cfg.act_quant == 0 else 1)
+    work["pre_reorder"] = dict(bytes=T * k * 4 + tok_local * H * 2 + (T * H * 2 if cfg.act_quant == 0 else 0)
                                + M * H + a_scale_bytes13 + T * k * 4 + cfg.m_cap * 4 + (El + 1) * 4,
                                flops=0)
     work["gemm_w13"] = dict(bytes=M * H + a_scale_bytes13 + b13 + M * 2 * I * 2 + (El + 1) * 4,
@@ -222,8 +225,9 @@ def main():
         del gbuf
     stages = STAGES
     seg = buf.seg_indptr.cpu().numpy()
+    tokens_local = int((buf.src2dst.view(cfg.T, -1) >= 0).any(dim=1).sum())
     work, M, nonempty = algorithmic_work(cfg, seg, buf.a13_scale.numel() * 4, buf.a2_scale.numel() * 4,
-                                         s13.numel(), s2.numel())
+                                         s13.numel(), s2.numel(), tokens_local)
     stage_stats = {}
     for name in stages:
         t = stage_ms[name] * 1e-3

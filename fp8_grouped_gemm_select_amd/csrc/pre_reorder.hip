@@ -25,7 +25,7 @@ namespace moe {
 namespace {
 
 constexpr int kChunkPairs = 64;
-constexpr int kRegIters = 8;   // rows up to 8192 wide stay in registers
+constexpr int kRegIters = 7;   // rows up to 7168 wide stay in registers
 constexpr int kAmaxBlocks = 1024;
 
 struct PreWs {
@@ -365,7 +365,8 @@ __device__ __forceinline__ void scatter_token(
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256) void pr_scatter_quant_kernel(
+// five waves per SIMD: the row buffer (7 x 32 bytes per lane) and the rest fit 96 VGPRs
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void pr_scatter_quant_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ ids, int64_t T, int H, int topk,
     LocalMap map, int num_local, int64_t nch, const int32_t* __restrict__ offs,
     const int32_t* __restrict__ tot, int32_t* __restrict__ seg, int32_t* __restrict__ src2dst,
