@@ -1,6 +1,6 @@
 // Stage 1: the fused gate (scoring, grouped top-k, renormalisation, routed
-// scaling factor): sixteen lanes per token where the expert count allows it,
-// else one wavefront per token.
+// scaling factor): thirty-two or sixteen lanes per token where the expert count
+// allows it, else one wavefront per token.
 //
 // Follows "[1/2] sgl-kernel: Fuse routed scaling factor into select_experts"
 // (sglang PR #8364), Motivation and Modifications: the scaling factor is
@@ -209,22 +209,51 @@ __global__ __launch_bounds__(256) void select_experts_kernel(
     }
 }
 
-// Sixteen lanes per token, four tokens per wave (E = 16 * EPL, EPL in {4, 8, 16}):
-// the serial part of the selection (one round per chosen expert) runs once for
-// four tokens, and every cross-lane step stays inside a 16-lane DPP row.
-// Lane rl = lane % 16 of row lane / 16 owns experts rl * EPL + i. Same
-// per-expert arithmetic and ordering rules as select_experts_kernel; a group
-// spans LPG = (E / n_group) / EPL lanes (1, 2, 4, 8 or 16) when n_group > 1.
-template <int EPL, int SCORE>
+// A row of LPT lanes: maximum / sum over it, in every lane (LPT 16 or 32):
+// DPP inside each 16-lane row, then a permlane16 swap between row pairs.
+template <int LPT>
+__device__ __forceinline__ float row_max(float m) {
+    m = fmaxf(m, dpp<kDppXor1>(m));
+    m = fmaxf(m, dpp<kDppXor2>(m));
+    m = fmaxf(m, dpp<kDppHalfMirror>(m));
+    m = fmaxf(m, dpp<kDppMirror>(m));
+    if (LPT == 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    return m;
+}
+template <int LPT>
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    v += dpp<kDppMirror>(v);
+    if (LPT == 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return v;
+}
+
+// LPT lanes per token, 64 / LPT tokens per wave (E = LPT * EPL, EPL in {4, 8,
+// 16}): the serial part of the selection (one round per chosen expert) runs
+// once for all the wave's tokens, and every cross-lane step stays inside the
+// token's lanes (DPP rows, one permlane16 swap for LPT 32). Lane rl = lane %
+// LPT of its token owns experts rl * EPL + i. Same per-expert arithmetic and
+// ordering rules as select_experts_kernel; a group spans LPG = (E / n_group) /
+// EPL lanes (1, 2, 4, 8 or 16) when n_group > 1.
+template <int EPL, int SCORE, int LPT>
 __global__ __launch_bounds__(256) void select_rows_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int topk,
     int n_group, int topk_group, int renormalize, float rsf, int apply_rsf,
     int n_shared, float shared_weight, int stride, int32_t* __restrict__ ids_out,
     float* __restrict__ w_out) {
-    constexpr int E = 16 * EPL;
+    constexpr int E = LPT * EPL;
+    constexpr int TPB = 256 / LPT;  // tokens per block
     static_assert(EPL <= 16, "the allowed set is a 16-bit mask per lane");
-    const int lane = threadIdx.x & 63, rl = lane & 15, rbase = lane & 48;
-    const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int lane = threadIdx.x & 63, rl = lane & (LPT - 1), rbase = lane & (64 - LPT);
+    const int64_t t = (int64_t)blockIdx.x * TPB + (threadIdx.x / LPT);
     const bool active = t < T;
     const float* l = logits + (active ? t : 0) * E + rl * EPL;
     // the bias loads go to the logits row when there is no bias (masked below),
@@ -291,13 +320,9 @@ __global__ __launch_bounds__(256) void select_rows_kernel(
             lsc = take ? sc[i] : lsc;
             li = take ? i : li;
         }
-        float m = li >= 0 ? lb : -INFINITY;
-        m = fmaxf(m, dpp<kDppXor1>(m));
-        m = fmaxf(m, dpp<kDppXor2>(m));
-        m = fmaxf(m, dpp<kDppHalfMirror>(m));
-        m = fmaxf(m, dpp<kDppMirror>(m));
+        const float m = row_max<LPT>(li >= 0 ? lb : -INFINITY);
         const uint64_t owners = __ballot(li >= 0 && lb == m);
-        const uint32_t sub = (uint32_t)(owners >> rbase) & 0xFFFFu;
+        const uint32_t sub = (uint32_t)(owners >> rbase) & (LPT == 32 ? 0xFFFFFFFFu : 0xFFFFu);
         const int owner = sub ? __builtin_ctz(sub) : 0;
         const int wi = __shfl(li, rbase + owner, MOE_WAVE);
         const float wsc = __shfl(lsc, rbase + owner, MOE_WAVE);
@@ -309,31 +334,19 @@ __global__ __launch_bounds__(256) void select_rows_kernel(
 
     float v = 0.0f, all = 1.0f;
     if (SCORE == MOE_SCORE_SOFTMAX) {
-        float m = lmax;
-        m = fmaxf(m, dpp<kDppXor1>(m));
-        m = fmaxf(m, dpp<kDppXor2>(m));
-        m = fmaxf(m, dpp<kDppHalfMirror>(m));
-        m = fmaxf(m, dpp<kDppMirror>(m));
+        const float m = row_max<LPT>(lmax);
         if (rl < topk) v = exp_fixed(my_sc - m);
         if (!renormalize) {
             float part = 0.0f;
 #pragma unroll
             for (int i = 0; i < EPL; ++i)
                 if (active) part += exp_fixed(sc[i] - m);
-            part += dpp<kDppXor1>(part);
-            part += dpp<kDppXor2>(part);
-            part += dpp<kDppHalfMirror>(part);
-            part += dpp<kDppMirror>(part);
-            all = part;
+            all = row_sum<LPT>(part);
         }
     } else if (rl < topk) {
         v = my_sc;
     }
-    float sel = rl < topk ? v : 0.0f;
-    sel += dpp<kDppXor1>(sel);
-    sel += dpp<kDppXor2>(sel);
-    sel += dpp<kDppHalfMirror>(sel);
-    sel += dpp<kDppMirror>(sel);
+    const float sel = row_sum<LPT>(rl < topk ? v : 0.0f);
     float w = v / (renormalize ? sel : all);
     if (apply_rsf) w = w * rsf;
     if (active && rl < topk) {
@@ -376,10 +389,26 @@ int launch_select_experts(const float* logits, const float* correction_bias, int
     const bool rows_ok = (epl16 == 4 || epl16 == 8 || epl16 == 16) && topk + n_shared <= 16 &&
                          (!correction_bias || aligned16(correction_bias)) &&
                          (n_group == 1 || (gsz % epl16 == 0 && 16 % (gsz / epl16) == 0));
+    // thirty-two lanes per token for E = 256 (eight experts per lane)
+    const bool rows32 = E == 256 && topk + n_shared <= 32 &&
+                        (!correction_bias || aligned16(correction_bias)) &&
+                        (n_group == 1 || (gsz % 8 == 0 && gsz / 8 <= 16 && 32 % (gsz / 8) == 0));
+    if (rows32) {
+        const dim3 g32((unsigned)ceil_div(T, 8)), b32(256);
+        if (score_fn == MOE_SCORE_SIGMOID)
+            hipLaunchKernelGGL((select_rows_kernel<8, MOE_SCORE_SIGMOID, 32>), g32, b32, 0, s, logits, correction_bias,
+                               T, topk, n_group, topk_group, renormalize, routed_scaling_factor, apply_rsf,
+                               n_shared, shared_weight, topk + n_shared, topk_ids, topk_weights);
+        else
+            hipLaunchKernelGGL((select_rows_kernel<8, MOE_SCORE_SOFTMAX, 32>), g32, b32, 0, s, logits, correction_bias,
+                               T, topk, n_group, topk_group, renormalize, routed_scaling_factor, apply_rsf,
+                               n_shared, shared_weight, topk + n_shared, topk_ids, topk_weights);
+        return launch_status();
+    }
     if (rows_ok) {
         const dim3 g16((unsigned)ceil_div(T, 16)), b16(256);
 #define MOE_LAUNCH_ROWS(EPL, SC)                                                                  \
-    hipLaunchKernelGGL((select_rows_kernel<EPL, SC>), g16, b16, 0, s, logits, correction_bias, T, topk, \
+    hipLaunchKernelGGL((select_rows_kernel<EPL, SC, 16>), g16, b16, 0, s, logits, correction_bias, T, topk, \
                        n_group, topk_group, renormalize, routed_scaling_factor, apply_rsf,       \
                        n_shared, shared_weight, topk + n_shared, topk_ids, topk_weights)
         if (score_fn == MOE_SCORE_SIGMOID) {
