@@ -197,7 +197,7 @@ def time_layer(cfg, inp, steps, warmup, moe, torch, dev, graph=False):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs the layer on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
