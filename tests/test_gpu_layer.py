@@ -251,3 +251,56 @@ def test_layer_full_size_sampled_tokens(name):
           f"{(err - tol).max():.3g}", flush=True)
     assert flips <= 0.02 * total
     assert np.all(err <= tol + extra), "output outside tolerance plus the propagated differences"
+
+
+def _random_cfg(i):
+    """Seeded random small layer: expert count, top-k, grouping, EP slice, shapes
+    and quantisation modes drawn over the supported combinations."""
+    g = np.random.default_rng(1000 + i)
+    E = int(g.choice([8, 16, 32, 64, 128, 256]))
+    sigmoid = g.random() < 0.65
+    if sigmoid:
+        groups = [d for d in (2, 4, 8, 16) if E % d == 0 and E // d >= 2]
+        n_group = int(g.choice(groups)) if g.random() < 0.75 else 1
+        topk_group = int(g.integers(1, n_group + 1))
+        topk = int(g.integers(1, min(8, topk_group * (E // n_group)) + 1))
+    else:
+        n_group, topk_group = 1, 1
+        topk = int(g.integers(1, min(8, E) + 1))
+    num_local = int(g.integers(1, E + 1))
+    expert_start = int(g.integers(0, E - num_local + 1))
+    act_quant, w_quant = [(W.ACT_PER_TENSOR, W.W_PER_EXPERT), (W.ACT_PER_TOKEN, W.W_PER_CHANNEL),
+                          (W.ACT_PER_TOKEN, W.W_PER_EXPERT), (W.ACT_PER_TOKEN, W.W_BLOCK),
+                          (W.ACT_PER_GROUP, W.W_BLOCK), (W.ACT_PER_GROUP, W.W_PER_CHANNEL)][int(g.integers(0, 6))]
+    H = int(g.choice([128, 256, 384, 512]))
+    I = int(g.choice([128, 256])) if w_quant == W.W_BLOCK or act_quant == W.ACT_PER_GROUP else int(g.choice([64, 128, 192, 256]))
+    T = int(g.integers(1, 160))
+    return W.MoEConfig(name=f"random{i}", T=T, H=H, I=I, E=E, topk=topk, num_local=num_local,
+                       expert_start=expert_start, score_fn=W.SCORE_SIGMOID if sigmoid else W.SCORE_SOFTMAX,
+                       n_group=n_group, topk_group=topk_group, renormalize=int(g.integers(0, 2)),
+                       rsf=float(g.choice([1.0, 2.5])), apply_rsf=int(g.integers(0, 2)),
+                       use_bias=sigmoid and bool(g.integers(0, 2)), act_quant=act_quant, w_quant=w_quant)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_layer_random_configs(i):
+    """Sixteen seeded random layers over expert counts (8-256, so both stage-1
+    layouts), grouping, EP slices, shapes and every supported scale-mode pair:
+    ids, permutation and stage-2 codes bit-exact, the output within tolerance."""
+    cfg = _random_cfg(i)
+    print(f"layer random {i}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.topk} "
+          f"groups={cfg.n_group}/{cfg.topk_group} local=[{cfg.expert_start},{cfg.expert_start + cfg.num_local}) "
+          f"score={cfg.score_fn} act={cfg.act_quant} w={cfg.w_quant} renorm={cfg.renormalize} "
+          f"rsf={cfg.rsf}/{cfg.apply_rsf} bias={cfg.use_bias}", flush=True)
+    inp = W.gen_layer_inputs(cfg, seed=i)
+    ref = oracle.layer(inp)
+    buf = run_layer(inp)
+    assert np.array_equal(buf.topk_ids.cpu().numpy(), ref["ids"])
+    w = buf.topk_weights.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(w - ref["weights"]) <= 4e-6 * np.abs(ref["weights"]) + 1e-12)
+    assert np.array_equal(buf.seg_indptr.cpu().numpy(), ref["seg_indptr"])
+    assert np.array_equal(buf.src2dst.cpu().numpy(), ref["src2dst"])
+    M = int(ref["seg_indptr"][-1])
+    assert np.array_equal(buf.dst2src.cpu().numpy(), ref["dst2src"])
+    assert np.array_equal(buf.a13.cpu().numpy()[:M], ref["a13"][:M])
+    G.assert_close_layer(G.bf16_bits(buf.out), ref["out"], what="layer output")
