@@ -3,10 +3,15 @@
     python -m fp8_grouped_gemm_select_amd.profsum trace  TRACE_CSV --workload W --command CMD --out MD
     python -m fp8_grouped_gemm_select_amd.profsum traffic FETCH_CSV WRITE_CSV --calib-bytes N
                                                   --workload W --command CMD --out-json J --out-md MD
+    python -m fp8_grouped_gemm_select_amd.profsum counters CSV [CSV ...] --workload W
+                                                  --command CMD [--command CMD] --out MD
 
 `trace` reads a `--kernel-trace` CSV (one row per dispatch) and writes a
 markdown table of calls / total / average duration per kernel, with the two
 grouped-GEMM launches of a layer pass (w13 first, then w2) split apart.
+
+`counters` summarises any other `--pmc` CSVs per stage (MFMA busy share,
+FP8 matrix flop, L2 hit rate).
 
 `traffic` reads two `--pmc` counter CSVs of the same command (FETCH_SIZE, then
 WRITE_SIZE, both in KiB per dispatch) and converts them to bytes per launch of
@@ -117,6 +122,83 @@ def trace_md(path, workload, command):
     return "\n".join(lines) + "\n"
 
 
+SIMDS = 1024  # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8      # GRBM_GUI_ACTIVE reads the sum over the 8 XCDs
+
+
+def load_counters(paths):
+    """Every (dispatch, counter) value of one or more `--pmc` CSVs, stages
+    assigned per file (the w13 / w2 split by GEMM order within each run), and
+    the layer pass each dispatch belongs to (a pass starts at stage 1)."""
+    per = {}
+    for path in paths:
+        names = sorted({r["Counter_Name"] for r in _rows(path)})
+        for name in names:
+            for d in load_counter(path, name):
+                if d["stage"] is None:
+                    continue
+                key = (path, d["id"])
+                e = per.setdefault(key, {"stage": d["stage"]})
+                e[name] = d["value"]
+        for r in _rows(path):
+            key = (path, int(r["Dispatch_Id"]))
+            if key in per and "dur_us" not in per[key] and r.get("End_Timestamp"):
+                per[key]["dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    out, npass, cur_path = [], -1, None
+    for (path, _), e in sorted(per.items(), key=lambda kv: kv[0]):
+        if path != cur_path:
+            cur_path, npass = path, -1
+        if e["stage"] == "select":
+            npass += 1
+        out.append(dict(e, run=(path, npass)))
+    return out
+
+
+def counters_md(paths, workload, commands):
+    """Per stage: mean counter values per dispatch and the figures derived from
+    them (MFMA busy share of SIMD cycles, FP8 matrix flop from the MOPS counter,
+    L2 hit rate)."""
+    ds = load_counters(paths)
+    lines = [f"# Hardware counters per stage, workload `{workload}`", "",
+             "Commands (from /tmp on the GPU host, repository at $REPO):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "Median over layer passes of each stage's dispatches summed. GRBM_GUI_ACTIVE reads the sum over the "
+              f"{XCDS} XCDs, so one XCD's busy cycles are a {XCDS}th of it (it also counts a fixed "
+              "few microseconds around each dispatch, which dominates the short kernels). MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+              f"(GRBM_GUI_ACTIVE / {XCDS} x {SIMDS} SIMDs); FP8 flop = SQ_INSTS_VALU_MFMA_MOPS_F8 x "
+              "512 (the MFMA work issued, padded tiles included); L2 hit = TCC_HIT / (TCC_HIT + "
+              "TCC_MISS).", "",
+              "| stage | dispatches | µs | MFMA busy | FP8 GFLOP issued | L2 hit |",
+              "|---|---|---|---|---|---|"]
+    for st in STAGES:
+        rows = [d for d in ds if d["stage"] == st]
+        if not rows:
+            continue
+        # per layer pass: the stage's dispatches summed (stage 2 has three kernels)
+        by_pass = {}
+        for d in rows:
+            acc = by_pass.setdefault(d["run"], {})
+            for k, v in d.items():
+                if k not in ("stage", "run"):
+                    acc[k] = acc.get(k, 0.0) + v
+
+        def mean(name):  # the median over passes (the first pass can stray)
+            v = sorted(p[name] for p in by_pass.values() if name in p)
+            return v[len(v) // 2] if v else None
+
+        gui, busy = mean("GRBM_GUI_ACTIVE"), mean("SQ_VALU_MFMA_BUSY_CYCLES")
+        mops, hit, miss = mean("SQ_INSTS_VALU_MFMA_MOPS_F8"), mean("TCC_HIT_sum"), mean("TCC_MISS_sum")
+        dur = mean("dur_us")
+        n = max(sum(1 for d in rows if k in d) for k in rows[0] if k not in ("stage", "dur_us", "run"))
+        xcd_cycles = gui / XCDS if gui else None
+        util = f"{100 * busy / (xcd_cycles * SIMDS):.1f} %" if xcd_cycles and busy is not None else "—"
+        gf = f"{mops * 512 / 1e9:.1f}" if mops is not None else "—"
+        l2 = f"{100 * hit / (hit + miss):.1f} %" if hit is not None and miss is not None and hit + miss else "—"
+        ds_us = f"{dur:.1f}" if dur else "—"
+        lines.append(f"| {st} | {n} | {ds_us} | {util} | {gf} | {l2} |")
+    return "\n".join(lines) + "\n"
+
+
 def stats_md(path):
     """The profiler's own per-kernel summary (`--stats`), names shortened."""
     lines = ["", "rocprofv3 `--stats` kernel summary of the same run:", "",
@@ -219,7 +301,16 @@ def main(argv=None):
     b.add_argument("--command", required=True)
     b.add_argument("--out-json", required=True)
     b.add_argument("--out-md", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--command", action="append", required=True)
+    c.add_argument("--out", required=True)
     args = p.parse_args(argv)
+    if args.cmd == "counters":
+        with open(args.out, "w") as f:
+            f.write(counters_md(args.csv, args.workload, args.command))
+        return
     if args.cmd == "trace":
         with open(args.out, "w") as f:
             f.write(trace_md(args.csv, args.workload, args.command))

@@ -70,3 +70,28 @@ def test_trace_table(tmp_path):
     assert "| gemm_w13 | 3 | 400.00 |" in md
     assert "| gemm_w2 | 3 | 200.00 |" in md
     assert "| pre_reorder | 3 | 50.00 |" in md
+
+
+def test_counter_table(tmp_path):
+    """MFMA busy over one XCD's share of GRBM_GUI_ACTIVE, FP8 flop from the MOPS
+    counter, L2 hit rate, and stage 2's kernels summed per layer pass."""
+    path = tmp_path / "c.csv"
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        did, t = 1, 0
+        for _ in range(3):  # three layer passes
+            for k, dur in zip(KERNELS, [10, 20, 30, 400, 40, 200, 50]):
+                gemm = "grouped_gemm" in k
+                vals = {"GRBM_GUI_ACTIVE": 8 * 1000, "SQ_VALU_MFMA_BUSY_CYCLES": 512 * 1000 if gemm else 0,
+                        "SQ_INSTS_VALU_MFMA_MOPS_F8": 2e6 if gemm else 0, "TCC_HIT_sum": 3, "TCC_MISS_sum": 1}
+                for name, v in vals.items():
+                    w.writerow({"Dispatch_Id": did, "Kernel_Name": k, "Counter_Name": name, "Counter_Value": v,
+                                "Start_Timestamp": t, "End_Timestamp": t + dur * 1000})
+                did += 1
+                t += dur * 1000 + 5
+    md = profsum.counters_md([str(path)], "tiny", ["cmd"])
+    # 512e3 busy cycles over (8e3 / 8 XCDs) x 1024 SIMDs = 50 %; 2e6 MOPS x 512 = 1.024 GFLOP
+    assert "| gemm_w13 | 3 | 400.0 | 50.0 % | 1.0 | 75.0 % |" in md
+    assert "| pre_reorder | 6 | 50.0 | 0.0 % | 0.0 | 75.0 % |" in md
