@@ -113,9 +113,10 @@ def trace_md(path, workload, command):
         lines.append(f"| `{k}` | {n} | {t:.1f} | {t / n:.2f} | {100 * t / total:.1f} |")
     lines += ["", "Per stage of the layer pass (grouped-GEMM launches split by position: w13 first, then w2):",
               "", "| stage | launches | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    n_pass = sum(1 for d in ds if d["stage"] == "select")
     for st in STAGES:
         v = [d["dur_us"] for d in ds if d["stage"] == st]
-        if st == "pre_reorder":  # several kernels per launch: sum per layer pass
+        if st == "pre_reorder" or len(v) > n_pass:  # several kernels per stage: sum per layer pass
             v = _per_pass_sums(ds, st)
         if v:
             lines.append(f"| {st} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
