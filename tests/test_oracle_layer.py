@@ -188,6 +188,54 @@ def test_grouped_gemm_k_tail_and_empty_experts():
     assert np.all(c[13:] == 0)
 
 
+
+_MODE_PAIRS = [(W.ACT_PER_TENSOR, W.W_PER_EXPERT), (W.ACT_PER_TOKEN, W.W_PER_EXPERT),
+               (W.ACT_PER_TOKEN, W.W_PER_CHANNEL), (W.ACT_PER_GROUP, W.W_BLOCK),
+               (W.ACT_PER_GROUP, W.W_PER_CHANNEL), (W.ACT_PER_TOKEN, W.W_BLOCK)]
+
+
+@pytest.mark.parametrize("act_quant,w_quant", _MODE_PAIRS)
+def test_grouped_gemm_rows_reproduces_exact_case(act_quant, w_quant):
+    """The sampled-row GEMM reproduces the exact-arithmetic case row by row (every
+    row of every segment, the padding rows past M as zeros)."""
+    a_q, sa, b_q, sb, seg, expect, m_cap = _exact_gemm_case(act_quant, w_quant)
+    rows = np.arange(m_cap)
+    c = oracle.grouped_gemm_rows(a_q, sa, act_quant, b_q, sb, w_quant, seg, rows)
+    M = int(seg[-1])
+    assert np.array_equal(c[:M], expect[:M])
+    assert np.all(c[M:] == 0)
+
+
+@pytest.mark.parametrize("act_quant,w_quant", _MODE_PAIRS)
+def test_grouped_gemm_rows_equals_full_gemm_at_boundaries(act_quant, w_quant):
+    """Random finite codes and scales on ragged segments with empty experts: the
+    rows on both sides of every segment boundary, random interior rows and rows
+    at or past M equal the whole-matrix oracle's rows bit for bit (rows outside
+    every segment are zeros there too). A wrong row-to-expert lookup at a
+    boundary or a scale read at the wrong row breaks the equality."""
+    g = np.random.default_rng(60 + 7 * act_quant + w_quant)
+    N, K = 160, 384
+    counts = np.array([0, 5, 1, 0, 17, 2, 0, 9])
+    E_l = len(counts)
+    seg = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(seg[-1])
+    m_cap = M + 6
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    a_q = finite[g.integers(0, len(finite), (m_cap, K))]
+    b_q = finite[g.integers(0, len(finite), (E_l, N, K))]
+    sa = g.uniform(0.5, 2.0, W.a_scale_numel(act_quant, m_cap, K)).astype(np.float32)
+    sb = g.uniform(0.5, 2.0, W.b_scale_numel(w_quant, E_l, N, K)).astype(np.float32)
+    full = oracle.grouped_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg)
+    edges = [r for e in range(E_l) if counts[e] > 0 for r in (seg[e], seg[e + 1] - 1)]
+    rows = np.array(sorted(set(edges)) + list(g.integers(0, M, 6)) + [M, M + 1, m_cap - 1],
+                    dtype=np.int64)
+    c = oracle.grouped_gemm_rows(a_q, sa, act_quant, b_q, sb, w_quant, seg, rows)
+    assert np.array_equal(c, full[rows])
+    assert np.all(c[-3:] == 0)
+    # the rows really are distinct data (a lookup that returned the wrong expert
+    # or scale row would not go unnoticed)
+    assert len({bytes(r) for r in c[:len(edges)]}) == len(edges)
+
 # ---- activation + requant -----------------------------------------------------
 
 @pytest.mark.parametrize("mode", [W.ACT_PER_TOKEN, W.ACT_PER_GROUP, W.ACT_PER_TENSOR])
