@@ -5,10 +5,13 @@ guard regions behind every output buffer.
 Every output tensor is allocated with a trailing guard region filled with a
 sentinel; ``check_guards`` fails if any kernel wrote past its buffer.
 """
+import functools
+
 import numpy as np
 import torch
 
 import fp8_grouped_gemm_select_amd as moe
+import workloads as W
 
 GUARD = 4096  # elements behind every output buffer
 SENTINEL = {torch.uint8: 0xA5, torch.int32: -123456789, torch.float32: float("nan"),
@@ -17,6 +20,14 @@ SENTINEL = {torch.uint8: 0xA5, torch.int32: -123456789, torch.float32: float("na
 
 def dev():
     return torch.device("cuda:0")
+
+
+@functools.lru_cache(maxsize=1)
+def layer_inputs(name, seed=0):
+    """Seeded inputs of a named workload, weights included. The last one drawn is
+    kept, so consecutive tests of one workload share a single draw of its
+    weights (the Mixtral-shaped experts alone are 1.4 GB of codes)."""
+    return W.gen_layer_inputs(W.CONFIGS[name], seed=seed)
 
 
 def up(a, dtype=None):

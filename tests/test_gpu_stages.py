@@ -265,23 +265,28 @@ def _rand_gemm(seed, counts, N, K, act_quant, w_quant, extra=7):
 
 def abs_products(a_q, sa, act_quant, b_q, sb, w_quant, seg, rows):
     """sum_k |a_hat[r,k] * b_hat[e,n,k]| for the given rows (fp64), the scale of the
-    fp32 summation error of either side."""
+    fp32 summation error of either side. Each expert's |b_hat| is formed once."""
     table = np.abs(oracle.e4m3_decode_table().astype(np.float64))
     sa = np.asarray(sa).reshape(-1)
     sb = np.asarray(sb).reshape(-1)
     m_cap, K = a_q.shape
     E_l, N, _ = b_q.shape
     KB, NB = -(-K // 128), -(-N // 128)
+    rows = np.asarray(rows)
     out = np.zeros((len(rows), N))
-    for i, r in enumerate(rows):
-        e = int(np.searchsorted(seg, r, side="right") - 1)
-        if act_quant == W.ACT_PER_TENSOR:
-            sa_row = np.full(K, sa[0], np.float64)
-        elif act_quant == W.ACT_PER_TOKEN:
-            sa_row = np.full(K, sa[r], np.float64)
-        else:
-            sa_row = np.repeat(sa[r * KB:(r + 1) * KB].astype(np.float64), 128)[:K]
-        a = table[a_q[r]] * np.abs(sa_row)
+    experts = np.searchsorted(seg, rows, side="right") - 1
+    for e in np.unique(experts):
+        idx = np.nonzero(experts == e)[0]
+        a = np.empty((len(idx), K))
+        for q, i in enumerate(idx):
+            r = int(rows[i])
+            if act_quant == W.ACT_PER_TENSOR:
+                sa_row = np.full(K, sa[0], np.float64)
+            elif act_quant == W.ACT_PER_TOKEN:
+                sa_row = np.full(K, sa[r], np.float64)
+            else:
+                sa_row = np.repeat(sa[r * KB:(r + 1) * KB].astype(np.float64), 128)[:K]
+            a[q] = table[a_q[r]] * np.abs(sa_row)
         bt = table[b_q[e]]
         if w_quant == W.W_PER_EXPERT:
             bt = bt * abs(float(sb[e]))
@@ -290,7 +295,8 @@ def abs_products(a_q, sa, act_quant, b_q, sb, w_quant, seg, rows):
         else:
             blk = np.abs(sb[e * NB * KB:(e + 1) * NB * KB].astype(np.float64)).reshape(NB, KB)
             bt = bt * np.repeat(np.repeat(blk, 128, 0), 128, 1)[:N, :K]
-        out[i] = bt @ a
+        out[idx] = a @ bt.T
+        del bt
     return out
 
 
@@ -316,11 +322,16 @@ def test_grouped_gemm_random(act_quant, w_quant, dims):
 
 
 @pytest.mark.parametrize("name,which", [("dsv3_prefill_ep", "w13"), ("dsv3_prefill_ep", "w2"),
-                                        ("mixtral", "w13"), ("skewed_block", "w2"),
-                                        ("dsv3_decode_ep", "w13")])
+                                        ("mixtral", "w13"), ("mixtral", "w2"),
+                                        ("skewed_block", "w13"), ("skewed_block", "w2"),
+                                        ("dsv3_decode_ep", "w13"), ("dsv3_decode_ep", "w2")])
 def test_grouped_gemm_full_size_sampled_rows(name, which):
-    """Full workload shapes in the benchmark's launch configuration; 48 sampled rows
-    (all N columns) recomputed by the oracle one row at a time."""
+    """Full workload shapes in the benchmark's launch configuration. Sampled rows
+    (all N columns) are recomputed by the oracle one row at a time: 44 random
+    rows, the first and last row, and the first and last row of every non-empty
+    expert segment (where a tile-table or row-scale indexing error would show).
+    The Mixtral w2 case is the longest K loop (K = 14336) with the per-tensor
+    activation scale."""
     cfg, inp, ids, _ = routed(name)
     m_cap = cfg.m_cap
     s2d, d2s, seg = oracle.permute(ids, cfg.expert_start, cfg.num_local, m_cap)
@@ -333,10 +344,13 @@ def test_grouped_gemm_full_size_sampled_rows(name, which):
         K, N = cfg.I, cfg.H
         a_q = g.integers(0, 0x7E, (m_cap, K)).astype(np.uint8) | (g.integers(0, 2, (m_cap, K)) * 0x80).astype(np.uint8)
         sa = g.uniform(1e-3, 4e-3, W.a_scale_numel(cfg.act_quant, m_cap, K)).astype(np.float32)
-    b_q, sb = W.gen_weights(cfg, which)
+    full = G.layer_inputs(name)
+    b_q, sb = (full.w13, full.w13_scale) if which == "w13" else (full.w2, full.w2_scale)
     print(f"grouped_gemm full {name} {which} M={M} N={N} K={K}", flush=True)
     c = G.run_gemm(a_q, sa, cfg.act_quant, b_q, sb, cfg.w_quant, seg)
-    rows = np.unique(np.concatenate([g.integers(0, M, 44), [0, M - 1], seg[1:-1][:2]]))
+    nonempty = np.nonzero(seg[1:] > seg[:-1])[0]
+    edges = np.concatenate([seg[nonempty], seg[nonempty + 1] - 1])
+    rows = np.unique(np.concatenate([g.integers(0, M, 44), [0, M - 1], edges]))
     rows = rows[rows < M]
     ref = oracle.grouped_gemm_rows(a_q, sa, cfg.act_quant, b_q, sb, cfg.w_quant, seg, rows)
     G.assert_close_layer(c[rows], ref, what="C rows")
@@ -437,7 +451,7 @@ def test_act_requant_full_size(name):
 
 # ---- stage 5 ------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["tiny", "dsv3_prefill_ep", "skewed_block"])
+@pytest.mark.parametrize("name", ["tiny", "dsv3_prefill_ep", "mixtral", "skewed_block"])
 def test_post_reorder(name):
     cfg, inp, ids, w = routed(name)
     s2d, d2s, seg = oracle.permute(ids, cfg.expert_start, cfg.num_local, cfg.m_cap)
