@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_INVALID_ARG, MOE_ERR_SHAPE = 0, -1, -2, -3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = -4, -5, -6
+MOE_NOALLOC_SCRATCH_BYTES = 8 << 20  # static scratch of moe_pre_reorder_quant_noalloc (moe.h)
 
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 ACT_PER_TENSOR, ACT_PER_TOKEN, ACT_PER_GROUP = 0, 1, 2
@@ -32,7 +33,8 @@ W_PER_EXPERT, W_PER_CHANNEL, W_BLOCK = 0, 1, 2
 EXPORTS = ["moe_select_experts", "moe_workspace_bytes", "moe_pre_reorder_quant",
            "moe_grouped_gemm_fp8", "moe_act_requant", "moe_post_reorder", "moe_status_string",
            "moe_router_select", "moe_select_experts_shared", "moe_pre_reorder_quant_shared",
-           "moe_grouped_gemm_mxfp4", "moe_router_workspace_bytes"]
+           "moe_grouped_gemm_mxfp4", "moe_router_workspace_bytes",
+           "moe_pre_reorder_quant_noalloc"]
 
 _lib = None
 
@@ -63,6 +65,9 @@ def load_library():
     lib.moe_pre_reorder_quant.restype = ctypes.c_int
     lib.moe_pre_reorder_quant.argtypes = [P, P, I64, I32, I32, I32, I32, I32, I64, P, P, I64,
                                           P, P, P, P, SZ, P]
+    lib.moe_pre_reorder_quant_noalloc.restype = ctypes.c_int
+    lib.moe_pre_reorder_quant_noalloc.argtypes = [P, P, I64, I32, I32, I32, I32, I32, I64, P, P,
+                                                  I64, P, P, P, P]
     lib.moe_grouped_gemm_fp8.restype = ctypes.c_int
     lib.moe_grouped_gemm_fp8.argtypes = [P, P, I64, I32, P, P, I64, I32, P, I32, I64, I32, I32,
                                          P, P]
@@ -233,6 +238,24 @@ def moe_pre_reorder_quant(x, topk_ids, a_q, a_scale, src2dst, dst2src, seg_indpt
         _ptr(seg_indptr), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(rc, "moe_pre_reorder_quant")
+
+
+def moe_pre_reorder_quant_noalloc(x, topk_ids, a_q, a_scale, src2dst, dst2src, seg_indptr, *,
+                                  expert_start, num_local, act_quant, stream=None):
+    """moe_pre_reorder_quant with the library's static scratch instead of a
+    workspace: nothing is allocated. Calls that overlap on one GPU race."""
+    _dtype(x, torch.bfloat16, name="x")
+    _dtype(topk_ids, torch.int32, name="topk_ids")
+    _dtype(a_q, torch.uint8, torch.float8_e4m3fn, name="a_q")
+    _dtype(a_scale, torch.float32, name="a_scale")
+    T, H = x.shape
+    topk = topk_ids.shape[1]
+    m_cap = a_q.shape[0]
+    rc = load_library().moe_pre_reorder_quant_noalloc(
+        _ptr(x), _ptr(topk_ids), T, H, topk, expert_start, num_local, act_quant, m_cap,
+        _ptr(a_q), _ptr(a_scale), a_scale.numel(), _ptr(src2dst), _ptr(dst2src),
+        _ptr(seg_indptr), _stream(stream))
+    _check(rc, "moe_pre_reorder_quant_noalloc")
 
 
 def moe_grouped_gemm_fp8(a_q, a_scale, b_q, b_scale, seg_indptr, c, *, act_quant, w_quant,

@@ -21,6 +21,8 @@
 //            local rows; the grid clears dst2src[M..m_cap).
 #include "common.h"
 
+#include <mutex>
+
 namespace moe {
 namespace {
 
@@ -496,4 +498,56 @@ extern "C" int moe_pre_reorder_quant_shared(const void* x_bf16, const int32_t* t
     return moe::pre_reorder_impl(x_bf16, topk_ids, T, H, topk, expert_start, num_routed, shared_base,
                                  n_shared, act_quant, m_cap, a_q, a_scale, a_scale_numel, src2dst,
                                  dst2src, seg_indptr, workspace, workspace_bytes, stream);
+}
+
+// ---- the variant that allocates nothing ------------------------------------------
+//
+// moe_pre_reorder_quant_noalloc runs the same three kernels with their scratch
+// (chunk counts, offsets, per-expert totals, amax partials, the per-tensor
+// scale) in `scratch`, a static device array that every GPU the library runs
+// on holds until the process ends. In host code the array's name is only a
+// host-side stand-in: the device address is taken with hipGetSymbolAddress on
+// the first call on each device (with that device current) and kept per device;
+// only that address reaches the kernels. The kernels write every scratch entry
+// they later read, so nothing needs clearing between calls; calls that overlap
+// on one GPU share the array and race.
+__device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace moe {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_pre_reorder_quant_noalloc(const void* x_bf16, const int32_t* topk_ids, int64_t T,
+                                             int32_t H, int32_t topk, int32_t expert_start,
+                                             int32_t num_local, int32_t act_quant, int64_t m_cap,
+                                             uint8_t* a_q, float* a_scale, int64_t a_scale_numel,
+                                             int32_t* src2dst, int32_t* dst2src, int32_t* seg_indptr,
+                                             void* stream) {
+    using namespace moe;
+    if (T < 0 || topk <= 0 || num_local < 0) return MOE_ERR_INVALID_ARG;
+    if (topk > 32 || num_local > 8192 || T * (int64_t)topk > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (pre_ws_bytes(T, topk, num_local) > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    const int rc = scratch_address(&ws);
+    if (rc != MOE_OK) return rc;
+    return pre_reorder_impl(x_bf16, topk_ids, T, H, topk, expert_start, num_local, 0, 0, act_quant,
+                            m_cap, a_q, a_scale, a_scale_numel, src2dst, dst2src, seg_indptr, ws,
+                            (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }

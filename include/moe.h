@@ -198,6 +198,26 @@ int moe_pre_reorder_quant(const void* x_bf16, const int32_t* topk_ids, int64_t T
                           void* stream);
 
 /*
+ * moe_pre_reorder_quant without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, results and checks as
+ * moe_pre_reorder_quant; the scratch lives in a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that each GPU holds until the process ends. The
+ * call allocates and frees nothing. Its scratch need is that of
+ * moe_workspace_bytes(T, topk, num_local) for this stage; a shape that needs
+ * more (about T * topk / 64 * num_local * 8 bytes) returns MOE_ERR_WORKSPACE
+ * before anything is enqueued. Calls on one GPU share the array: calls that
+ * overlap in time on the same GPU (two streams, two threads) race and give
+ * undefined results; calls in stream order are safe.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_pre_reorder_quant_noalloc(const void* x_bf16, const int32_t* topk_ids, int64_t T, int32_t H,
+                                  int32_t topk, int32_t expert_start, int32_t num_local,
+                                  int32_t act_quant, int64_t m_cap, uint8_t* a_q, float* a_scale,
+                                  int64_t a_scale_numel, int32_t* src2dst, int32_t* dst2src,
+                                  int32_t* seg_indptr, void* stream);
+
+/*
  * Stage 3 (and 5), the grouped FP8 GEMM over the local experts.
  * Source: "Fix one bug in the grouped-gemm triton kernel" (sglang PR #6772),
  * Highlights: without block quantisation the activation scale is loaded at the

@@ -96,6 +96,25 @@ def test_pre_reorder_rejects(lib):
     assert _pre(lib, x=ctypes.c_void_p(0x10002)) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_pre_reorder_noalloc_rejects_before_touching_the_device(lib):
+    """The allocation-free stage 2 refuses shapes whose scratch exceeds its static
+    array (and bad sizes) before any HIP call: these run without a GPU."""
+    f = lib.moe_pre_reorder_quant_noalloc
+    def call(T=16, topk=2, num_local=8):
+        return f(FAKE, FAKE, T, 128, topk, 0, num_local, 1, T * 2, FAKE, FAKE, T * 2, FAKE, FAKE,
+                 FAKE, None)
+    assert call(T=-1) == moe.MOE_ERR_INVALID_ARG
+    assert call(topk=0) == moe.MOE_ERR_INVALID_ARG
+    assert call(num_local=-1) == moe.MOE_ERR_INVALID_ARG
+    assert call(topk=33) == moe.MOE_ERR_UNSUPPORTED
+    # 1M tokens x 8 slots in chunks of 64, 256 local experts: ~256 MB of counts
+    assert call(T=1 << 20, topk=8, num_local=256) == moe.MOE_ERR_WORKSPACE
+    # the largest stage-2 scratch among the five workloads fits
+    assert moe.moe_workspace_bytes(16384, 8, 128) <= moe.MOE_NOALLOC_SCRATCH_BYTES
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == moe.MOE_NOALLOC_SCRATCH_BYTES
+
+
 def _gemm(lib, act=1, w=0, a_n=64, b_n=4, m_cap=64, N=128, K=256, num_local=4, seg=FAKE, c=FAKE):
     return lib.moe_grouped_gemm_fp8(FAKE, FAKE, a_n, act, FAKE, FAKE, b_n, w, seg, num_local,
                                     m_cap, N, K, c, None)
