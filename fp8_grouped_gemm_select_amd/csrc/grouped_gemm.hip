@@ -710,6 +710,235 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
     }
 }
 
+// ---- 256 x 256 tiles: eight waves (two per SIMD), two-stage LDS-DMA ring ----
+//
+// The block-scaled modes (1 x 128 activation groups or 128 x 128 weight blocks)
+// when the segments can fill 256-row tiles. There every 128-deep MFMA result is
+// added into the fp32 accumulators on the VALU with its own factor, so the
+// register-prefetch schedule of the 128 x 256 kernel does not fit (it spills);
+// a 256 x 256 tile halves the barriers and loads per flop instead. A step moves
+// 64 KB (256 A rows and 256 B rows of 128 bytes) for 16.8 MFLOP, about 31 bytes
+// per clock at one CU's MFMA rate through its L2 -> LDS path (which sustains
+// about 50).
+//
+// Waves 2 (M) x 4 (N). Wave (wm, wn) owns the 64 columns wn*64.. (four 16-column
+// MFMA blocks) and the eight 16-row blocks 2i + wm (i = 0..7): the row blocks
+// alternate between the two wave rows, so a tile with fewer valid rows keeps
+// both busy. Row blocks past the tile's valid rows skip their operand reads and
+// MFMAs, and A DMA instructions whose eight rows are all past them are not
+// issued. Accumulators: 8 x 4 blocks x 4 values = 128 fp32 per lane.
+//
+// Step k of a tile (stage s): wait for this wave's DMA of the step, one barrier
+// (the stage is complete; every wave is done with the other stage, so it is
+// free), then the DMA of the next step into the other stage -- the next step of
+// this tile, or the first step of the block's next tile -- interleaved with the
+// first four row blocks, then the MFMAs: the four B operands read once, A block
+// i+1 read while block i's four MFMAs run. After the last step a barrier frees
+// its stage, which then stages the bf16 tile for 16-byte row stores while the
+// next tile's first step loads into the other one.
+constexpr int GT = 256;                   // tile rows = tile columns
+constexpr int kGStageA = GT * 128;        // 32 KB
+constexpr int kGStage = 2 * kGStageA;     // 64 KB: A rows then B rows
+constexpr int kGDma = GT * 128 / 1024 / 8;  // 1 KB DMA instructions per wave per operand per step: 4
+
+struct GTile {
+    int e, row0, row_end, n0, a_rows, b_rows, sa_row;
+    const uint8_t* a_g;
+    const uint8_t* b_g;
+    uint32_t a_off[kGDma], b_off[kGDma];
+};
+
+template <bool KDEP>
+__global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_256_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, int act_quant,
+    const uint8_t* __restrict__ B, const float* __restrict__ sb, int w_quant,
+    const int32_t* __restrict__ seg_in, int num_local, int64_t m_cap, int N, int K,
+    uint16_t* __restrict__ C) {
+    __shared__ __align__(16) uint8_t lds[2 * kGStage];
+    __shared__ int s_seg[kMaxLocal + 1];
+    __shared__ int s_tstart[kMaxLocal + 1];
+    __shared__ int scan_scratch[17];
+    __shared__ float s_sa[2][GT];  // activation group scales of a step's rows (per-group mode)
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid >> 2, wn = wid & 3;
+    const int KB = K / MOE_QB;
+    const int NB = (N + MOE_QB - 1) / MOE_QB;
+    const int nk = K / 128;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const void*)lds;
+    const bool group_act = KDEP && act_quant == MOE_ACT_PER_GROUP;
+    const bool block_w = KDEP && w_quant == MOE_W_BLOCK;
+
+    const int total = build_tile_table<GT, GT>(seg_in, num_local, m_cap, N, s_seg, s_tstart, scan_scratch);
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd_blocks = gridDim.x >> 3;
+    const int per_xcd = (total + 7) / 8;
+    const int lt_begin = xcd * per_xcd;
+    const int lt_end = lt_begin + per_xcd < total ? lt_begin + per_xcd : total;
+
+    // DMA instruction q = wid + 8 i of an operand fills its rows 8 q .. 8 q + 7
+    // (lane l: row 8 q + l / 8, LDS chunk position l % 8, which holds global
+    // chunk (l % 8) ^ perm8(row)); rows past the valid ones re-read the last one
+    auto setup = [&](int lt) {
+        const TileCoord tc = tile_coord<GT, GT>(lt, s_seg, s_tstart, num_local);
+        GTile t;
+        t.e = __builtin_amdgcn_readfirstlane(tc.e);
+        t.row0 = __builtin_amdgcn_readfirstlane(tc.row0);
+        t.row_end = __builtin_amdgcn_readfirstlane(tc.row_end);
+        t.n0 = __builtin_amdgcn_readfirstlane(tc.n0);
+        t.a_rows = tc.row_end - tc.row0;
+        t.b_rows = N - tc.n0 < GT ? N - tc.n0 : GT;
+#pragma unroll
+        for (int i = 0; i < kGDma; ++i) {
+            const int r = (wid + 8 * i) * 8 + (lane >> 3);
+            const int ga = r < t.a_rows ? r : t.a_rows - 1;
+            const int gb = r < t.b_rows ? r : t.b_rows - 1;
+            const uint32_t chunk = (uint32_t)((((lane & 7) ^ perm8(r)) << 4));
+            t.a_off[i] = (uint32_t)ga * (uint32_t)K + chunk;
+            t.b_off[i] = (uint32_t)gb * (uint32_t)K + chunk;
+        }
+        t.a_g = A + (int64_t)t.row0 * K;
+        t.b_g = B + ((int64_t)t.e * N + t.n0) * K;
+        t.sa_row = t.row0 + ((tid & (GT - 1)) < t.a_rows ? (tid & (GT - 1)) : t.a_rows - 1);
+        return t;
+    };
+    // part i (0..3) of the DMA of K step k of tile t into stage st: this wave's
+    // A and B instruction wid + 8 i
+    auto issue_part = [&](const GTile& t, int k, int st, int i) {
+        const uint32_t base = lds0 + (uint32_t)(st * kGStage) + (uint32_t)((wid + 8 * i) * 1024);
+        if ((wid + 8 * i) * 8 < t.a_rows)
+            dma16(uniform_ptr(t.a_g + k * 128), t.a_off[i], __builtin_amdgcn_readfirstlane(base));
+        if ((wid + 8 * i) * 8 < t.b_rows)
+            dma16(uniform_ptr(t.b_g + k * 128), t.b_off[i], __builtin_amdgcn_readfirstlane(base + kGStageA));
+    };
+
+    int lt = lt_begin + slot;
+    if (lt >= lt_end) return;  // the whole block has no tile
+
+    GTile cur = setup(lt);
+    float q = 0.f;  // this thread's activation group scale of the next step (per-group mode)
+    if (group_act) q = sa[(int64_t)cur.sa_row * KB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_part(cur, 0, 0, i);
+    int s = 0;  // stage of the current step
+
+    while (true) {
+        const int lt_next = lt + per_xcd_blocks;
+        const bool has_next = lt_next < lt_end;
+        GTile nxt = cur;
+        if (has_next) nxt = setup(lt_next);
+        const bool col_ok0 = wn * 64 < cur.b_rows;  // the wave has columns in this tile
+
+        v4f acc[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+        for (int k = 0; k < nk; ++k) {
+            wait_vmcnt<0>();
+            if (group_act && tid < GT) s_sa[s][tid] = q;
+            __syncthreads();  // stage s complete; stage s ^ 1 free
+            // what the next step in this block's sequence loads into stage s ^ 1
+            const bool more = k + 1 < nk;
+            const GTile& tn = more ? cur : nxt;
+            const int kn = more ? k + 1 : 0;
+            const bool issue = more || has_next;
+            if (group_act && issue) q = sa[(int64_t)tn.sa_row * KB + kn];
+            const int nb_w = (cur.n0 + wn * 64) / MOE_QB < NB ? (cur.n0 + wn * 64) / MOE_QB : NB - 1;
+            const float sbv = block_w ? sb[((int64_t)cur.e * NB + nb_w) * KB + k] : 1.0f;
+
+            const uint8_t* la = lds + s * kGStage;
+            const uint8_t* lb = la + kGStageA;
+            v8i bfr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bfr[j] = lds_operand(lb, wn * 64 + j * 16 + (lane & 15), lane);
+            v8i af = lds_operand(la, wm * 16 + (lane & 15), lane);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i < 4 && issue) issue_part(tn, kn, s ^ 1, i);
+                const int rb = 2 * i + wm;
+                if (rb * 16 < cur.a_rows && col_ok0) {
+                    v8i an = af;
+                    if (i + 1 < 8 && (rb + 2) * 16 < cur.a_rows)
+                        an = lds_operand(la, (rb + 2) * 16 + (lane & 15), lane);
+                    if constexpr (!KDEP) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                bfr[j], af, acc[i][j], 0, 0, 0, 0, 0, 0);
+                    } else {
+                        const float f = (group_act ? s_sa[s][rb * 16 + (lane & 15)] : 1.0f) * sbv;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                bfr[j], af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) acc[i][j][v] = acc[i][j][v] + t[v] * f;
+                        }
+                    }
+                    af = an;
+                }
+            }
+            s ^= 1;
+        }
+        // s is the stage of the next tile's first step; s ^ 1 held this tile's last
+        __syncthreads();  // every wave is done reading stage s ^ 1
+
+        // ---- epilogue: scales, bf16 into stage s ^ 1 (8 KB per wave), 16-byte
+        // row stores, in two halves of four row blocks ----
+        float srow[8], scol[4][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = cur.row0 + (2 * i + wm) * 16 + (lane & 15);
+            srow[i] = group_act ? 1.0f : (act_quant == MOE_ACT_PER_TENSOR ? sa[0] : sa[r < cur.row_end ? r : cur.row0]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int n = cur.n0 + wn * 64 + j * 16 + (lane >> 4) * 4 + v;
+                scol[j][v] = block_w ? 1.0f : (w_quant == MOE_W_PER_EXPERT ? sb[cur.e] : sb[(int64_t)cur.e * N + (n < N ? n : N - 1)]);
+            }
+        uint8_t* ep = lds + (s ^ 1) * kGStage + wid * (64 * 128);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int i = 4 * h + ii;
+                const int rl = ii * 16 + (lane & 15);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int cl = j * 16 + (lane >> 4) * 4;
+                    float hv[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) hv[v] = acc[i][j][v] * (srow[i] * scol[j][v]);
+                    *(uint2*)(ep + ep_off(rl, cl >> 3) + (cl & 7) * 2) =
+                        make_uint2(bf16x2_rne(hv[0], hv[1]), bf16x2_rne(hv[2], hv[3]));
+                }
+            }
+            // the staging area is the wave's own: its LDS writes are complete (in
+            // order, one wave) before its lanes read each other's values
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int rl = t * 8 + (lane >> 3), qc = lane & 7;
+                const int r = cur.row0 + (2 * (4 * h + (rl >> 4)) + wm) * 16 + (rl & 15);
+                const int n = cur.n0 + wn * 64 + qc * 8;
+                const uint4 v = *(const uint4*)(ep + ep_off(rl, qc));
+                if (r < cur.row_end && n < N) *(uint4*)(C + (int64_t)r * N + n) = v;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // the half is read back before it is overwritten
+            __builtin_amdgcn_wave_barrier();
+        }
+        if (!has_next) break;
+        cur = nxt;
+        lt = lt_next;
+    }
+    wait_vmcnt<0>();
+}
+
 // ---- FP4 weights, 256-deep K steps: 128 x 256 tiles, two-stage DMA ring ----
 //
 // With MXFP4 weights a 128-deep K step moves 64 bytes per weight row, half a
@@ -947,6 +1176,20 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a_q, const float* a_scale, in
     if (!aligned16(a_q) || !aligned16(b_q) || !aligned16(c_bf16)) return MOE_ERR_INVALID_ARG;
 
     (void)hipGetLastError();
+    const bool kdep_modes = act_quant == MOE_ACT_PER_GROUP || w_quant == MOE_W_BLOCK;
+    if (kdep_modes && K % 128 == 0 && (int64_t)K * GT < ((int64_t)1 << 32) && m_cap >= (int64_t)128 * num_local) {
+        // block-scaled modes with segments that could average 128 rows or more
+        // per local expert (chosen from the sizes alone; M stays on the device):
+        // 256 x 256 tiles
+        const int64_t upper = (ceil_div(m_cap, GT) + num_local) * ceil_div(N, GT);
+        int64_t g = (int64_t)device_cu_count();
+        if (g > ceil_div(upper, 8) * 8) g = ceil_div(upper, 8) * 8;
+        g = ceil_div(g < 8 ? 8 : g, 8) * 8;
+        hipLaunchKernelGGL((grouped_gemm_256_kernel<true>), dim3((unsigned)g), dim3(kDThreads), 0,
+                           (hipStream_t)stream, a_q, a_scale, act_quant, b_q, b_scale, w_quant, seg_indptr,
+                           num_local, m_cap, N, K, (uint16_t*)c_bf16);
+        return launch_status();
+    }
     if (K % DBK == 0 && (int64_t)K * DBN < ((int64_t)1 << 32)) {
         // large tiles, LDS-DMA pipeline: one block per CU
         const int64_t upper = (ceil_div(m_cap, DBM) + num_local) * ceil_div(N, DBN);

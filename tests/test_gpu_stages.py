@@ -247,6 +247,55 @@ def test_grouped_gemm_exact_case(act_quant, w_quant):
     assert np.array_equal(c[:M], expect[:M])
 
 
+# Cases with m_cap at least 128 rows per local expert, where the library takes
+# the 256 x 256 tile kernel for the block-scaled modes (the others keep the
+# 128 x 256 one): segments of every size around the 8-row DMA instructions, the
+# 16-row MFMA blocks and the 128- and 256-row tiles (empty ones too), and column
+# counts that leave a partial column tile.
+BIG_COUNTS = (1, 15, 16, 17, 0, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300)
+ALL_MODES = [(W.ACT_PER_TENSOR, W.W_PER_EXPERT), (W.ACT_PER_TOKEN, W.W_PER_EXPERT),
+             (W.ACT_PER_TOKEN, W.W_PER_CHANNEL), (W.ACT_PER_GROUP, W.W_BLOCK),
+             (W.ACT_PER_GROUP, W.W_PER_CHANNEL), (W.ACT_PER_TOKEN, W.W_BLOCK)]
+
+
+@pytest.mark.parametrize("act_quant,w_quant", ALL_MODES)
+def test_grouped_gemm_exact_case_256_tiles(act_quant, w_quant):
+    """The exact-arithmetic case with m_cap at least 128 rows per expert (the
+    256 x 256 tile kernel in the block-scaled modes): segments longer than a
+    tile, one row, one full tile, and a partial column tile; bit-exact."""
+    counts, N = (300, 0, 17, 256, 1), 384
+    m_cap_min = 128 * len(counts)
+    a_q, sa, b_q, sb, seg, expect, m_cap = _exact_gemm_case(act_quant, w_quant, counts=counts, N=N,
+                                                            extra=m_cap_min - sum(counts) + 9)
+    assert m_cap >= m_cap_min
+    print(f"grouped_gemm exact 256-row tiles act={act_quant} w={w_quant}", flush=True)
+    c = G.run_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg)
+    M = seg[-1]
+    assert np.array_equal(c[:M], expect[:M])
+
+
+@pytest.mark.parametrize("act_quant,w_quant", ALL_MODES)
+@pytest.mark.parametrize("N,K", [(256, 256), (384, 512), (160, 128)])
+def test_grouped_gemm_random_256_tiles(act_quant, w_quant, N, K):
+    """Random finite codes with m_cap at least 128 rows per expert (the 256 x 256
+    tile kernel in the block-scaled modes), every segment size around the row
+    boundaries: within one bf16 step plus both sides' summation bounds."""
+    if w_quant == W.W_BLOCK and N % 128:
+        N = 128 * -(-N // 128)
+    extra = 128 * len(BIG_COUNTS) - sum(BIG_COUNTS) + 13
+    a_q, sa, b_q, sb, seg = _rand_gemm(9, BIG_COUNTS, N, K, act_quant, w_quant, extra=extra)
+    assert a_q.shape[0] >= 128 * len(BIG_COUNTS)
+    print(f"grouped_gemm random 256-row tiles N={N} K={K} act={act_quant} w={w_quant}", flush=True)
+    ref = oracle.grouped_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg)
+    c = G.run_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg)
+    M = seg[-1]
+    G.assert_close_layer(c[:M], ref[:M], what="C")
+    rows = np.arange(M)
+    worst = G.assert_sum_close(c[:M], ref[:M], abs_products(a_q, sa, act_quant, b_q, sb, w_quant, seg, rows),
+                               K, what="C")
+    print(f"worst |diff| beyond one ulp, relative to sum|products|: {worst:.3g}")
+
+
 def _rand_gemm(seed, counts, N, K, act_quant, w_quant, extra=7):
     g = np.random.default_rng(seed)
     counts = np.asarray(counts)

@@ -86,12 +86,12 @@ def test_pre_reorder_quant_scales_and_roundtrip(mode):
 
 # ---- grouped GEMM: exact-arithmetic case ------------------------------------
 
-def _exact_gemm_case(act_quant, w_quant, seed=0):
+def _exact_gemm_case(act_quant, w_quant, seed=0, counts=(37, 0, 90, 21), N=256, K=256, extra=11):
     g = np.random.default_rng(30 + seed)
-    E_l, N, K = 4, 256, 256
-    counts = np.array([37, 0, 90, 21])
+    counts = np.asarray(counts)
+    E_l = len(counts)
     seg = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    m_cap = int(seg[-1]) + 11
+    m_cap = int(seg[-1]) + extra
     codes = np.array([0x38, 0xB8, 0x00], dtype=np.uint8)      # +1, -1, 0
     a_q = codes[g.integers(0, 3, (m_cap, K))]
     b_q = codes[g.integers(0, 3, (E_l, N, K))]
