@@ -48,6 +48,8 @@ def parse():
                    help="tokens in the oracle's timed sample (0: per-workload default)")
     p.add_argument("--no-graph", action="store_true",
                    help="time the headline from eager passes only (no HIP graph; for counter runs)")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the on-box ceilings (streaming copy and read, FP8 MFMA loop)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after the run, copy this many MiB once (a plain copy kernel for counter calibration)")
     return p.parse_args()
@@ -290,6 +292,14 @@ def main():
             torch.cuda.empty_cache()
             result["next_rows"]["fp4_layer"] = time_fp4_layer(W.CONFIGS[fp4_name], args, moe, W, torch, dev)
 
+    if not args.no_ceilings:
+        ceil = measure_ceilings(torch, dev)
+        result["ceilings"] = ceil
+        meas = ceil["hbm_read_GBps"] if roof["bound"] == "hbm" else ceil["fp8_mfma_TFLOPs"]
+        roof["measured_peak"] = meas
+        roof["frac_of_measured"] = round(roof["achieved"] / meas, 4)
+        gemm["frac_of_measured_mfma"] = round(gemm["tflops"] / ceil["fp8_mfma_TFLOPs"], 4)
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -373,6 +383,57 @@ def time_router_select(cfg, inp, args, moe, W, torch, dev):
                 TFLOPs=round(flops / t / 1e12, 1), bf16_mfma_frac=round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4),
                 algorithmic_bytes=int(byts), flops=int(flops),
                 note="bf16 router projection x @ wg^T + stage 1, timed on its own, not in value")
+
+
+def measure_ceilings(torch, dev, nbytes=2 << 30, mfma_iters=2000, reps=5):
+    """What this GPU reaches with plain kernels (libmoe_ceilings.so): a streaming
+    copy and a streaming read of `nbytes` (HBM GB/s; the copy counts its bytes
+    read and written) and a loop of independent 16x16x128 FP8 MFMAs on every CU
+    at two waves per SIMD (TFLOP/s, and the shader clock it held). Each is the
+    mean of `reps` timed launches after two untimed ones."""
+    import ctypes
+    from fp8_grouped_gemm_select_amd import _build
+    lib = ctypes.CDLL(_build.CEIL_LIB)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.ceil_stream_copy.argtypes = [P, P, I64, P]
+    lib.ceil_stream_read.argtypes = [P, I64, P, P]
+    lib.ceil_mfma_loop.argtypes = [I32, P, P, P]
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty_like(src)
+    small = torch.zeros(64, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(launch):
+        for _ in range(2):
+            launch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            launch()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    def check(rc):
+        if rc < 0:
+            raise RuntimeError(f"ceiling kernel launch failed ({rc})")
+        return rc
+
+    t_copy = timed(lambda: check(lib.ceil_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream)))
+    t_read = timed(lambda: check(lib.ceil_stream_read(src.data_ptr(), nbytes, small.data_ptr(), stream)))
+    blocks = [0]
+    t_mfma = timed(lambda: blocks.__setitem__(0, check(lib.ceil_mfma_loop(
+        mfma_iters, small.data_ptr(), small[8:].data_ptr(), stream))))
+    clk = small[8:10].cpu().numpy()
+    flops = float(blocks[0]) * 8 * mfma_iters * 16 * 65536
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(hbm_copy_GBps=round(2 * nbytes / t_copy / 1e9, 1), hbm_read_GBps=round(nbytes / t_read / 1e9, 1),
+                fp8_mfma_TFLOPs=round(flops / t_mfma / 1e12, 1),
+                mfma_clock_GHz=round(float(clk[0]) / (float(clk[1]) / 100e6) / 1e9, 3),
+                note=f"plain kernels on this GPU: copy and read of {nbytes >> 20} MiB, "
+                     f"16x16x128 FP8 MFMA loop (two waves per SIMD); not in value")
 
 
 def measured_traffic(workload, stage):

@@ -1,0 +1,99 @@
+// On-box ceilings that the benchmark sets its roofline fractions beside: a
+// streaming copy and a streaming read of device memory (HBM bandwidth as a plain
+// kernel reaches it) and a loop of independent FP8 MFMAs (the matrix cores'
+// rate at the clock they hold under that load). Not part of the layer's ABI;
+// built into libmoe_ceilings.so, which only the benchmark loads.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                   int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// four independent 16-byte loads in flight per thread; the xor keeps them live
+__global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                   uint32_t* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t x = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        x ^= a.x ^ a.w ^ b.y ^ b.z ^ c.x ^ c.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) x ^= src[i].x;
+    if (x == 0x9E3779B9u) out[0] = x;  // practically never: keeps the loads
+}
+
+// 16 independent v_mfma_f32_16x16x128_f8f6f4 accumulators per wave, two waves
+// per SIMD; the first wave records the shader-clock and 100 MHz counters around
+// its loop
+__global__ __launch_bounds__(512) void mfma_kernel(int iters, float* __restrict__ out,
+                                                   uint64_t* __restrict__ clk) {
+    v4f acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    v8i a, b;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        a[q] = 0x38383838 ^ (int)(threadIdx.x * (q + 1));
+        b[q] = 0x30303030 + q;
+    }
+    const uint64_t t0 = __builtin_readcyclecounter(), r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[i], 0, 0, 0, 0, 0, 0);
+    }
+    const uint64_t t1 = __builtin_readcyclecounter(), r1 = __builtin_amdgcn_s_memrealtime();
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+    if (s == 1.2345f) out[0] = s;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        clk[0] = t1 - t0;
+        clk[1] = r1 - r0;
+    }
+}
+
+int cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    return n;
+}
+
+}  // namespace
+
+// dst[0, bytes) = src[0, bytes); bytes a multiple of 16, both 16-byte aligned
+extern "C" int ceil_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    if (!src || !dst || bytes <= 0 || bytes % 16 || ((uintptr_t)src | (uintptr_t)dst) % 16) return -2;
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)(cus() * 8)), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4*)src, (uint4*)dst, bytes / 16);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// reads src[0, bytes); out4: 4 writable bytes (touched only by an improbable xor)
+extern "C" int ceil_stream_read(const void* src, int64_t bytes, void* out4, void* stream) {
+    if (!src || !out4 || bytes <= 0 || bytes % 16 || (uintptr_t)src % 16) return -2;
+    hipLaunchKernelGGL(read_kernel, dim3((unsigned)(cus() * 8)), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4*)src, bytes / 16, (uint32_t*)out4);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// one 512-thread block per CU, `iters` rounds of 16 MFMAs per wave: flops =
+// blocks * 8 * iters * 16 * 65536; out: 4 writable bytes; clk: two uint64
+// (shader clocks and 100 MHz ticks of the first wave's loop). Returns blocks.
+extern "C" int ceil_mfma_loop(int32_t iters, void* out, void* clk, void* stream) {
+    if (iters <= 0 || !out || !clk) return -2;
+    const int blocks = cus();
+    hipLaunchKernelGGL(mfma_kernel, dim3((unsigned)blocks), dim3(512), 0, (hipStream_t)stream, iters,
+                       (float*)out, (uint64_t*)clk);
+    return hipGetLastError() == hipSuccess ? blocks : -6;
+}

@@ -45,6 +45,9 @@ def _load():
     lib.oracle_bf16_rne_f64.argtypes = [ctypes.c_double]
     lib.oracle_exp_ref.restype = F32
     lib.oracle_exp_ref.argtypes = [F32]
+    lib.oracle_math_vec.restype = ctypes.c_int
+    lib.oracle_math_vec.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p]
     lib.oracle_sigmoid.restype = F32
     lib.oracle_sigmoid.argtypes = [F32]
     lib.oracle_silu_mul_bf16.restype = ctypes.c_uint16
@@ -143,6 +146,14 @@ def sigmoid(x: float) -> float:
 
 def silu_mul_bf16(g: float, u: float) -> int:
     return int(_load().oracle_silu_mul_bf16(float(g), float(u)))
+
+
+def math_vec(x):
+    """exp_ref, sigmoid and the fp32 SiLU x / (1 + exp_ref(-x)) of every fp32 in x."""
+    x = _c(np.asarray(x, dtype=np.float32).reshape(-1), np.float32)
+    e, sg, sl = (np.empty_like(x) for _ in range(3))
+    _check(_load().oracle_math_vec(_p(x), len(x), _p(e), _p(sg), _p(sl)), "math_vec")
+    return e, sg, sl
 
 
 # ---- stages ---------------------------------------------------------------

@@ -167,6 +167,19 @@ uint16_t oracle_silu_mul_bf16(float g, float u) {
     return oracle_bf16_rne(s * u);
 }
 
+/* The scalar definitions above over an array (for dense device comparisons):
+ * exp_out[i] = exp_ref(x[i]), sig_out[i] = sigmoid(x[i]) and silu_out[i] =
+ * x[i] / (1 + exp_ref(-x[i])), the fp32 SiLU before the multiply by up. */
+int oracle_math_vec(const float* x, int64_t n, float* exp_out, float* sig_out, float* silu_out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        exp_out[i] = oracle_exp_ref(x[i]);
+        sig_out[i] = oracle_sigmoid(x[i]);
+        silu_out[i] = x[i] / (1.0f + oracle_exp_ref(-x[i]));
+    }
+    return 0;
+}
+
 /* Dynamic FP8 scale of a group of values with maximum magnitude amax:
  * scale = amax'/448 (stored, used to dequantise) and inv = 448/amax' (used to
  * quantise), with amax' = max(amax, 1e-10) so that all-zero rows stay finite. */

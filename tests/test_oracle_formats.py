@@ -191,3 +191,17 @@ def test_silu_mul_bf16_close_to_exact():
         assert abs(int(h) - int(rb)) <= 1 or (ref == 0.0), (a, b)
         exact += int(h) == int(rb)
     assert exact >= 0.99 * len(gs)
+
+
+def test_math_vec_is_the_scalar_definitions():
+    """The array form used for dense device comparisons evaluates exactly the
+    pinned scalar exp_ref and sigmoid, and SiLU as x / (1 + exp_ref(-x))."""
+    g = np.random.default_rng(3)
+    x = np.concatenate([np.linspace(-90, 90, 2001), g.uniform(-88, 88, 2000),
+                        [0.0, -0.0, 1e-30, -1e-30]]).astype(np.float32)
+    e, sg, sl = oracle.math_vec(x)
+    for v, a, b, c in zip(x, e, sg, sl):
+        assert np.float32(oracle.exp_ref(float(v))) == a
+        assert np.float32(oracle.sigmoid(float(v))) == b
+        d = np.float32(1.0) + np.float32(oracle.exp_ref(float(-v)))
+        assert np.float32(v) / d == c or (np.isnan(c) and np.isnan(np.float32(v) / d))
