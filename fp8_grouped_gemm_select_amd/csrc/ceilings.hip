@@ -71,10 +71,18 @@ int cus() {
 
 }  // namespace
 
+// Grids of short-lived blocks (each thread four 16-byte elements): on this GPU
+// they stream faster than a persistent grid of a few blocks per CU (measured
+// 5.3-5.5 against 4.5-4.8 TB/s for a copy).
+static unsigned stream_grid(int64_t n16) {
+    const int64_t g = (n16 + 1023) / 1024;
+    return (unsigned)(g > 0x7FFFFFFF ? 0x7FFFFFFF : (g < 1 ? 1 : g));
+}
+
 // dst[0, bytes) = src[0, bytes); bytes a multiple of 16, both 16-byte aligned
 extern "C" int ceil_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
     if (!src || !dst || bytes <= 0 || bytes % 16 || ((uintptr_t)src | (uintptr_t)dst) % 16) return -2;
-    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)(cus() * 8)), dim3(256), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL(copy_kernel, dim3(stream_grid(bytes / 16)), dim3(256), 0, (hipStream_t)stream,
                        (const uint4*)src, (uint4*)dst, bytes / 16);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
@@ -82,7 +90,7 @@ extern "C" int ceil_stream_copy(const void* src, void* dst, int64_t bytes, void*
 // reads src[0, bytes); out4: 4 writable bytes (touched only by an improbable xor)
 extern "C" int ceil_stream_read(const void* src, int64_t bytes, void* out4, void* stream) {
     if (!src || !out4 || bytes <= 0 || bytes % 16 || (uintptr_t)src % 16) return -2;
-    hipLaunchKernelGGL(read_kernel, dim3((unsigned)(cus() * 8)), dim3(256), 0, (hipStream_t)stream,
+    hipLaunchKernelGGL(read_kernel, dim3(stream_grid(bytes / 16)), dim3(256), 0, (hipStream_t)stream,
                        (const uint4*)src, bytes / 16, (uint32_t*)out4);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
