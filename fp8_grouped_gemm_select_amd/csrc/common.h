@@ -191,6 +191,15 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32
                  : "memory");
 }
 
+// dma16 with the nontemporal hint: for data read once (streamed weights), so
+// that it does not displace lines that are read again.
+__device__ __forceinline__ void dma16_nt(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds_base)
+                 : "memory");
+}
+
 // One 4-byte global -> LDS DMA per lane, to LDS address lds_base + 4 * lane.
 __device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"

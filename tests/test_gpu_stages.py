@@ -296,6 +296,49 @@ def test_grouped_gemm_random_256_tiles(act_quant, w_quant, N, K):
     print(f"worst |diff| beyond one ulp, relative to sum|products|: {worst:.3g}")
 
 
+# Cases with m_cap at most 32 rows per local expert, K a multiple of 1024 and no
+# K-dependent scale, where the library streams each expert's weights once (one
+# block per expert and 64-column slice, 16 rows of the expert per pass): one-pass
+# segments (1, 2, 3, 5, 16 rows), two- and three-pass ones (17, 33, 48), empty
+# experts, and column counts that leave a partial 64-column slice.
+SMALL_COUNTS = (3, 0, 17, 33, 1, 16, 0, 48, 5, 2)
+PLAIN_MODES = [(W.ACT_PER_TENSOR, W.W_PER_EXPERT), (W.ACT_PER_TOKEN, W.W_PER_EXPERT),
+               (W.ACT_PER_TOKEN, W.W_PER_CHANNEL), (W.ACT_PER_TENSOR, W.W_PER_CHANNEL)]
+
+
+@pytest.mark.parametrize("act_quant,w_quant", PLAIN_MODES)
+def test_grouped_gemm_exact_case_streaming(act_quant, w_quant):
+    """The exact-arithmetic case on the weight-streaming path; bit-exact."""
+    counts, N, K = SMALL_COUNTS, 80, 1024
+    m_cap_max = 32 * len(counts)
+    a_q, sa, b_q, sb, seg, expect, m_cap = _exact_gemm_case(act_quant, w_quant, counts=counts, N=N, K=K,
+                                                            extra=m_cap_max - sum(counts))
+    assert m_cap <= m_cap_max
+    print(f"grouped_gemm exact streaming act={act_quant} w={w_quant}", flush=True)
+    c = G.run_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg)
+    M = seg[-1]
+    assert np.array_equal(c[:M], expect[:M])
+
+
+@pytest.mark.parametrize("act_quant,w_quant", PLAIN_MODES)
+@pytest.mark.parametrize("N,K", [(272, 2048), (64, 1024), (1040, 3072)])
+def test_grouped_gemm_random_streaming(act_quant, w_quant, N, K):
+    """Random finite codes on the weight-streaming path: within one bf16 step
+    plus both sides' summation bounds."""
+    extra = 32 * len(SMALL_COUNTS) - sum(SMALL_COUNTS)
+    a_q, sa, b_q, sb, seg = _rand_gemm(11, SMALL_COUNTS, N, K, act_quant, w_quant, extra=extra)
+    assert a_q.shape[0] <= 32 * len(SMALL_COUNTS)
+    print(f"grouped_gemm random streaming N={N} K={K} act={act_quant} w={w_quant}", flush=True)
+    ref = oracle.grouped_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg)
+    c = G.run_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg)
+    M = seg[-1]
+    G.assert_close_layer(c[:M], ref[:M], what="C")
+    rows = np.arange(M)
+    worst = G.assert_sum_close(c[:M], ref[:M], abs_products(a_q, sa, act_quant, b_q, sb, w_quant, seg, rows),
+                               K, what="C")
+    print(f"worst |diff| beyond one ulp, relative to sum|products|: {worst:.3g}")
+
+
 def _rand_gemm(seed, counts, N, K, act_quant, w_quant, extra=7):
     g = np.random.default_rng(seed)
     counts = np.asarray(counts)
