@@ -1352,9 +1352,9 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a_q, const float* a_scale, in
 
     (void)hipGetLastError();
     const bool kdep_modes = act_quant == MOE_ACT_PER_GROUP || w_quant == MOE_W_BLOCK;
-    if (!kdep_modes && K % 128 == 0 && K / 128 >= SSTAGES && m_cap <= (int64_t)32 * num_local &&
+    if (!kdep_modes && K % 128 == 0 && K / 128 >= SSTAGES && m_cap <= (int64_t)64 * num_local &&
         (int64_t)K * SC < ((int64_t)1 << 32) && (int64_t)num_local * N * 4 < ((int64_t)1 << 32)) {
-        // few rows per expert (at most 32 on average even if every row slot is
+        // few rows per expert (at most 64 on average even if every row slot is
         // filled): stream each expert's weights once
         const int64_t upper = (ceil_div(m_cap, SM) + num_local) * ceil_div(N, SC);
         int64_t g = 2 * (int64_t)device_cu_count();

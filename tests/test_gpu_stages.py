@@ -296,7 +296,7 @@ def test_grouped_gemm_random_256_tiles(act_quant, w_quant, N, K):
     print(f"worst |diff| beyond one ulp, relative to sum|products|: {worst:.3g}")
 
 
-# Cases with m_cap at most 32 rows per local expert, K a multiple of 1024 and no
+# Cases with m_cap at most 64 rows per local expert, K a multiple of 1024 and no
 # K-dependent scale, where the library streams each expert's weights once (one
 # block per expert and 64-column slice, 16 rows of the expert per pass): one-pass
 # segments (1, 2, 3, 5, 16 rows), two- and three-pass ones (17, 33, 48), empty
