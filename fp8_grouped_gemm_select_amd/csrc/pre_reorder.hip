@@ -195,6 +195,71 @@ __global__ __launch_bounds__(256) void pr_scan_kernel(const int32_t* __restrict_
     }
 }
 
+// ---- count + scan in one block (few pairs) ---------------------------------------
+// The results of pr_count_kernel followed by pr_scan_kernel, in one launch, when
+// there are at most kFusedChunks chunks and the expert x chunk count table fits
+// in LDS (a decode batch): wave w ranks chunks w, w + 16, ... exactly as the
+// count kernel does, the table stays in LDS, and thread e then scans expert e's
+// row of it. The per-tensor amax partials (written by an earlier launch) are
+// reduced by the whole block.
+constexpr int kFusedChunks = 64;
+constexpr int kFusedTable = 8192;
+
+__global__ __launch_bounds__(1024) void pr_count_scan_kernel(const int32_t* __restrict__ ids, int64_t F,
+                                                             LocalMap map, int num_local, int nch,
+                                                             int32_t* __restrict__ src2dst,
+                                                             int32_t* __restrict__ offs,
+                                                             int32_t* __restrict__ tot,
+                                                             const float* __restrict__ amax_part,
+                                                             int n_part, int per_tensor,
+                                                             float* __restrict__ a_scale,
+                                                             float* __restrict__ tscale) {
+    __shared__ int32_t cnt[kFusedTable];
+    __shared__ float red[16];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < num_local * nch; i += 1024) cnt[i] = 0;
+    __syncthreads();
+    for (int c = w; c < nch; c += 16) {
+        const int64_t f = (int64_t)c * kChunkPairs + lane;
+        const int e = f < F ? local_of(ids[f], map) : -1;
+        int below = 0, all = 0;
+#pragma unroll
+        for (int j = 0; j < 64; ++j) {
+            const int ej = __builtin_amdgcn_readlane(e, j);
+            const bool m = ej == e;
+            below += (m && j < lane) ? 1 : 0;
+            all += m ? 1 : 0;
+        }
+        if (e >= 0 && below == all - 1) cnt[e * nch + c] = all;
+        if (f < F) src2dst[f] = e >= 0 ? below : -1;
+    }
+    __syncthreads();
+    for (int e = tid; e < num_local; e += 1024) {
+        int run = 0;
+        for (int c = 0; c < nch; ++c) {
+            offs[(int64_t)e * nch + c] = run;
+            run += cnt[e * nch + c];
+        }
+        tot[e] = run;
+    }
+    if (per_tensor) {
+        float m = 0.0f;
+        for (int i = tid; i < n_part; i += 1024) m = fmaxf(m, amax_part[i]);
+        m = wave_max(m);
+        if (lane == 0) red[w] = m;
+        __syncthreads();
+        if (tid == 0) {
+            float a = red[0];
+            for (int q = 1; q < 16; ++q) a = fmaxf(a, red[q]);
+            float sc, inv;
+            dyn_scale(a, sc, inv);
+            a_scale[0] = sc;
+            tscale[0] = sc;
+            tscale[1] = inv;
+        }
+    }
+}
+
 // First row of local expert e (exclusive prefix sum of the totals, for each
 // lane's own e; lanes with e < 0 get 0) and, in `total`, M = all local pairs.
 // Wave-uniform loop over the totals in groups of 64.
@@ -445,10 +510,6 @@ static int pre_reorder_impl(const void* x_bf16, const int32_t* topk_ids, int64_t
     hipStream_t s = (hipStream_t)stream;
     const int64_t nch = n_chunks(T, topk);
     PreWs ws = pre_ws_carve(workspace, T, topk, num_local);
-    if (nch > 0 && num_local > 0)
-        hipLaunchKernelGGL(pr_count_kernel, dim3((unsigned)nch), dim3(64),
-                           sizeof(int32_t) * num_local, s, topk_ids, T * (int64_t)topk, map,
-                           num_local, nch, src2dst, ws.counts);
     const int per_tensor = act_quant == MOE_ACT_PER_TENSOR;
     const int64_t n16 = T * (int64_t)H / 16;
     int n_part = 0;
@@ -457,9 +518,19 @@ static int pre_reorder_impl(const void* x_bf16, const int32_t* topk_ids, int64_t
         hipLaunchKernelGGL(pr_amax_kernel, dim3(n_part), dim3(256), 0, s, (const uint4*)x_bf16,
                            n16, ws.amax_part);
     }
-    hipLaunchKernelGGL(pr_scan_kernel, dim3((unsigned)(num_local > 0 ? num_local : 1)), dim3(256), 0, s,
-                       ws.counts, ws.offs, nch, num_local, ws.tot, ws.amax_part, n_part, per_tensor,
-                       a_scale, ws.tscale);
+    if (nch <= kFusedChunks && (int64_t)num_local * nch <= kFusedTable) {
+        hipLaunchKernelGGL(pr_count_scan_kernel, dim3(1), dim3(1024), 0, s, topk_ids, T * (int64_t)topk, map,
+                           num_local, (int)nch, src2dst, ws.offs, ws.tot, ws.amax_part, n_part, per_tensor,
+                           a_scale, ws.tscale);
+    } else {
+        if (nch > 0 && num_local > 0)
+            hipLaunchKernelGGL(pr_count_kernel, dim3((unsigned)nch), dim3(64),
+                               sizeof(int32_t) * num_local, s, topk_ids, T * (int64_t)topk, map,
+                               num_local, nch, src2dst, ws.counts);
+        hipLaunchKernelGGL(pr_scan_kernel, dim3((unsigned)(num_local > 0 ? num_local : 1)), dim3(256), 0, s,
+                           ws.counts, ws.offs, nch, num_local, ws.tot, ws.amax_part, n_part, per_tensor,
+                           a_scale, ws.tscale);
+    }
     // The scatter grid also writes seg_indptr and clears dst2src[M..m_cap); it
     // always runs, with at least one block.
     const int64_t nblk = ceil_div(T, 4) > 0 ? ceil_div(T, 4) : 1;
