@@ -388,7 +388,8 @@ def time_router_select(cfg, inp, args, moe, W, torch, dev):
 def measure_ceilings(torch, dev, nbytes=2 << 30, mfma_iters=2000, reps=5):
     """What this GPU reaches with plain kernels (libmoe_ceilings.so): a streaming
     copy and a streaming read of `nbytes` (HBM GB/s; the copy counts its bytes
-    read and written) and a loop of independent 16x16x128 FP8 MFMAs on every CU
+    read and written; the read is timed with ordinary and with nontemporal loads
+    and the faster one is the ceiling) and a loop of independent 16x16x128 FP8 MFMAs on every CU
     at two waves per SIMD (TFLOP/s, and the shader clock it held). Each is the
     mean of `reps` timed launches after two untimed ones."""
     import ctypes
@@ -397,6 +398,7 @@ def measure_ceilings(torch, dev, nbytes=2 << 30, mfma_iters=2000, reps=5):
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.ceil_stream_copy.argtypes = [P, P, I64, P]
     lib.ceil_stream_read.argtypes = [P, I64, P, P]
+    lib.ceil_stream_read_nt.argtypes = [P, I64, P, P]
     lib.ceil_mfma_loop.argtypes = [I32, P, P, P]
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
     dst = torch.empty_like(src)
@@ -422,6 +424,7 @@ def measure_ceilings(torch, dev, nbytes=2 << 30, mfma_iters=2000, reps=5):
 
     t_copy = timed(lambda: check(lib.ceil_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream)))
     t_read = timed(lambda: check(lib.ceil_stream_read(src.data_ptr(), nbytes, small.data_ptr(), stream)))
+    t_read_nt = timed(lambda: check(lib.ceil_stream_read_nt(src.data_ptr(), nbytes, small.data_ptr(), stream)))
     blocks = [0]
     t_mfma = timed(lambda: blocks.__setitem__(0, check(lib.ceil_mfma_loop(
         mfma_iters, small.data_ptr(), small[8:].data_ptr(), stream))))
@@ -429,11 +432,15 @@ def measure_ceilings(torch, dev, nbytes=2 << 30, mfma_iters=2000, reps=5):
     flops = float(blocks[0]) * 8 * mfma_iters * 16 * 65536
     del src, dst
     torch.cuda.empty_cache()
-    return dict(hbm_copy_GBps=round(2 * nbytes / t_copy / 1e9, 1), hbm_read_GBps=round(nbytes / t_read / 1e9, 1),
+    return dict(hbm_copy_GBps=round(2 * nbytes / t_copy / 1e9, 1),
+                hbm_read_GBps=round(nbytes / min(t_read, t_read_nt) / 1e9, 1),
+                hbm_read_plain_GBps=round(nbytes / t_read / 1e9, 1),
+                hbm_read_nontemporal_GBps=round(nbytes / t_read_nt / 1e9, 1),
                 fp8_mfma_TFLOPs=round(flops / t_mfma / 1e12, 1),
                 mfma_clock_GHz=round(float(clk[0]) / (float(clk[1]) / 100e6) / 1e9, 3),
-                note=f"plain kernels on this GPU: copy and read of {nbytes >> 20} MiB, "
-                     f"16x16x128 FP8 MFMA loop (two waves per SIMD); not in value")
+                note=f"plain kernels on this GPU: copy and read of {nbytes >> 20} MiB (hbm_read_GBps: the "
+                     f"faster of ordinary and nontemporal loads), 16x16x128 FP8 MFMA loop (two waves per "
+                     f"SIMD); not in value")
 
 
 def measured_traffic(workload, stage):

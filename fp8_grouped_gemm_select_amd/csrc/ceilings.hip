@@ -31,6 +31,24 @@ __global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ src
     if (x == 0x9E3779B9u) out[0] = x;  // practically never: keeps the loads
 }
 
+// The same read with the nontemporal hint (data not kept in the caches): on
+// this GPU a stream read this way runs faster than with ordinary loads.
+typedef int v4i __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void read_nt_kernel(const v4i* __restrict__ src, int64_t n16,
+                                                      uint32_t* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    int x = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const v4i a = __builtin_nontemporal_load(src + i), b = __builtin_nontemporal_load(src + i + stride);
+        const v4i c = __builtin_nontemporal_load(src + i + 2 * stride);
+        const v4i d = __builtin_nontemporal_load(src + i + 3 * stride);
+        x ^= a[0] ^ a[3] ^ b[1] ^ b[2] ^ c[0] ^ c[1] ^ d[2] ^ d[3];
+    }
+    for (; i < n16; i += stride) x ^= __builtin_nontemporal_load(src + i)[0];
+    if ((uint32_t)x == 0x9E3779B9u) out[0] = (uint32_t)x;  // practically never: keeps the loads
+}
+
 // 16 independent v_mfma_f32_16x16x128_f8f6f4 accumulators per wave, two waves
 // per SIMD; the first wave records the shader-clock and 100 MHz counters around
 // its loop
@@ -92,6 +110,14 @@ extern "C" int ceil_stream_read(const void* src, int64_t bytes, void* out4, void
     if (!src || !out4 || bytes <= 0 || bytes % 16 || (uintptr_t)src % 16) return -2;
     hipLaunchKernelGGL(read_kernel, dim3(stream_grid(bytes / 16)), dim3(256), 0, (hipStream_t)stream,
                        (const uint4*)src, bytes / 16, (uint32_t*)out4);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// ceil_stream_read with nontemporal loads
+extern "C" int ceil_stream_read_nt(const void* src, int64_t bytes, void* out4, void* stream) {
+    if (!src || !out4 || bytes <= 0 || bytes % 16 || (uintptr_t)src % 16) return -2;
+    hipLaunchKernelGGL(read_nt_kernel, dim3(stream_grid(bytes / 16)), dim3(256), 0, (hipStream_t)stream,
+                       (const v4i*)src, bytes / 16, (uint32_t*)out4);
     return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

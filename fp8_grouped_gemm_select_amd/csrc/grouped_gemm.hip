@@ -1154,51 +1154,51 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_fp4_kernel(
 //
 // When every local expert holds a handful of rows (decode), a 128-row tile is
 // mostly padding and the GEMM's cost is reading each expert's weights once from
-// HBM. Here a unit is (expert, 16 of its rows, 64 output columns) over the
-// whole of K, listed like the tiles above (m fastest, so an expert's few-row
-// blocks of one column slice run side by side and share its weights in L2),
-// and a persistent block of four waves takes its XCD's units in turn.
+// HBM. Here a unit is (expert, 16 of its rows, 16 output columns) over the whole
+// of K, listed like the tiles above (m fastest, so an expert's 16-row blocks of
+// one column block run side by side and share its weights in L2), and every
+// wave of a persistent grid takes its XCD's units in turn on its own: once the
+// unit list is built no LDS and no barrier is shared between waves, so no wave
+// waits for another's loads.
 //
 // Weights cannot go straight into MFMA registers at full HBM rate: a 16x16x128
 // operand spreads one load instruction over 16 rows of 64 bytes, and 128-byte
-// row segments stream about a fifth faster. So every operand goes through LDS
-// by global_load_lds_dwordx4, eight rows of 128 bytes per instruction (the
-// weights with the nontemporal hint), into a ring of SSTAGES stages. A block's
-// units form one stream of K steps: step j + SSTAGES - 1 is issued while step j
-// is consumed, across unit boundaries, so the ring never drains between units.
-// Per step each wave issues exactly three DMA instructions: its own 16 weight
-// rows (two), plus one of the unit's 16 activation rows (waves 0-1) or of the
-// unit's epilogue scales (waves 2-3: the 16 row scales and the 64 column scales,
-// re-sent each step into one of two buffers by unit parity). A step: wait for
-// the wave's own loads of the step, one barrier (the stage is complete in LDS
-// and every wave is done with the stage the next issue overwrites), issue, one
-// MFMA B x A. After a unit's last step the wave scales, rounds to bf16 and
-// stores its 16 x 16 outputs.
-constexpr int SC = 64;                      // output columns per unit
-constexpr int SM = 16;                      // rows per unit
-constexpr int SSTAGES = 7;
-constexpr int kSStageB = SC * 128;          // 8 KB
+// row segments stream about a fifth faster. So both operands go through the
+// wave's own LDS ring by global_load_lds_dwordx4, eight rows of 128 bytes per
+// instruction (the weights with the nontemporal hint unless the expert has
+// more than 16 rows, whose row blocks share them through L2), SSTAGES stages of one K
+// step each. A wave's units form one stream of K steps: step j + SSTAGES - 1 is
+// issued while step j is consumed, across unit boundaries, so the ring never
+// drains between units. Per step the wave issues exactly kSDma DMA
+// instructions: its 16 weight rows (two), the unit's 16 activation rows (two;
+// rows past the unit's last one re-read it, from L2) and two 4-byte DMAs of the
+// unit's epilogue scales (16 row scales, 16 column scales; re-sent each step
+// into one of two buffers by unit parity). A step: wait for the step's loads,
+// issue the next, one MFMA B x A. After a unit's last step the wave scales,
+// rounds to bf16 and stores its 16 x 16 outputs.
+constexpr int SC = 16;                       // output columns per unit
+constexpr int SM = 16;                       // rows per unit
+constexpr int SSTAGES = 4;
+constexpr int kSStageB = SC * 128;           // 2 KB
 constexpr int kSStage = kSStageB + SM * 128;  // + 2 KB of activations
-constexpr int kSDma = 3;                    // DMA instructions per wave per step
+constexpr int kSDma = 6;                     // DMA instructions per wave per step
 
 // vmcnt wait: at most n steps of this wave's DMA (kSDma each) still in flight
 __device__ __forceinline__ void wait_steps(int n) {
     switch (n) {
         case 0: wait_vmcnt<0>(); break;
         case 1: wait_vmcnt<kSDma>(); break;
-        case 2: wait_vmcnt<2 * kSDma>(); break;
-        case 3: wait_vmcnt<3 * kSDma>(); break;
-        case 4: wait_vmcnt<4 * kSDma>(); break;
-        default: wait_vmcnt<(SSTAGES - 2) * kSDma>(); break;
+        default: wait_vmcnt<2 * kSDma>(); break;
     }
 }
-static_assert(SSTAGES - 2 == 5, "wait_steps covers 0 .. SSTAGES - 2 steps");
+static_assert(SSTAGES - 2 == 2, "wait_steps covers 0 .. SSTAGES - 2 steps");
 
 struct SUnit {
-    int e, row0, row_end, n0;
+    int row0, row_end, n0;
+    int shared_b;        // the expert has more than SM rows: other units read these weights too
     const uint8_t* a_g;  // first activation row of the unit
     const uint8_t* b_g;  // first weight row of the unit
-    uint32_t offb0, offb1, offx;  // this wave's per-lane DMA offsets (see setup)
+    uint32_t offb0, offb1, offa0, offa1, offsa, offsb;  // per-lane DMA offsets (see setup)
 };
 
 __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(
@@ -1206,8 +1206,8 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(
     const uint8_t* __restrict__ B, const float* __restrict__ sb, int w_quant,
     const int32_t* __restrict__ seg_in, int num_local, int64_t m_cap, int N, int K,
     uint16_t* __restrict__ C) {
-    __shared__ __align__(16) uint8_t lds[SSTAGES * kSStage];
-    __shared__ __align__(16) float s_scale[2][2 * SC];  // per unit parity: row scales (64 slots), column scales
+    __shared__ __align__(16) uint8_t lds[4][SSTAGES * kSStage];
+    __shared__ __align__(16) float s_scale[4][2][128];  // per wave, per unit parity: row scales, column scales
     __shared__ int s_seg[kMaxLocal + 1];
     __shared__ int s_tstart[kMaxLocal + 1];
     __shared__ int scan_scratch[17];
@@ -1215,72 +1215,68 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nk = K / 128;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(const void*)lds;
-    const uint32_t lds_sc = (uint32_t)(uintptr_t)(const void*)&s_scale[0][0];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const void*)&lds[wid][0];
+    const uint32_t lds_sc = (uint32_t)(uintptr_t)(const void*)&s_scale[wid][0][0];
 
     const int total = build_tile_table<SM, SC>(seg_in, num_local, m_cap, N, s_seg, s_tstart, scan_scratch);
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd_blocks = gridDim.x >> 3;
+    // this XCD's waves take its contiguous eighth of the units in turn
+    const int xcd = blockIdx.x & 7;
+    const int per_xcd_waves = (gridDim.x >> 3) * 4;
+    const int wx = (blockIdx.x >> 3) * 4 + wid;
     const int per_xcd = (total + 7) / 8;
-    const int lt_begin = xcd * per_xcd + slot;
+    const int lt_begin = xcd * per_xcd + wx;
     const int lt_end = xcd * per_xcd + per_xcd < total ? xcd * per_xcd + per_xcd : total;
     if (lt_begin >= lt_end) return;
-    const int n_units = (lt_end - lt_begin + per_xcd_blocks - 1) / per_xcd_blocks;
+    const int n_units = (lt_end - lt_begin + per_xcd_waves - 1) / per_xcd_waves;
     const int n_steps = n_units * nk;
 
-    // DMA offsets of unit u for this wave: waves 0-3 weight rows 16 w + 8 i +
-    // lane / 8 (i = 0, 1); waves 0-1 activation rows 8 w + lane / 8; waves 2-3
-    // one scale per lane. Row indices past the unit's valid rows re-read its last
-    // one; chunk lane % 8 of an LDS row holds global chunk (lane % 8) ^ perm8(row).
+    // DMA offsets of unit u: weight rows 8 i + lane / 8 (i = 0, 1) and activation
+    // rows likewise (past the unit's valid rows: its last one); chunk lane % 8 of
+    // an LDS row holds global chunk (lane % 8) ^ perm8(row). Scales: lane l the
+    // row scale of row l % 16 (clamped) and the column scale of column l % 16.
     auto setup = [&](int u) {
-        const TileCoord tc = tile_coord<SM, SC>(lt_begin + u * per_xcd_blocks, s_seg, s_tstart, num_local);
+        const TileCoord tc = tile_coord<SM, SC>(lt_begin + u * per_xcd_waves, s_seg, s_tstart, num_local);
         SUnit t;
-        t.e = tc.e;
         t.row0 = tc.row0;
         t.row_end = tc.row_end;
         t.n0 = tc.n0;
-        const int b_rows = N - tc.n0 < SC ? N - tc.n0 : SC;
+        t.shared_b = s_seg[tc.e + 1] - s_seg[tc.e] > SM;
         const int a_rows = tc.row_end - tc.row0;
         t.a_g = A + (int64_t)tc.row0 * K;
         t.b_g = B + ((int64_t)tc.e * N + tc.n0) * K;
-        const int c = lane & 7;
-        auto boff = [&](int r) {
-            const int g = r < b_rows ? r : b_rows - 1;
-            return (uint32_t)g * (uint32_t)K + (uint32_t)((c ^ perm8(r & 15)) << 4);
-        };
-        t.offb0 = boff(16 * wid + (lane >> 3));
-        t.offb1 = boff(16 * wid + 8 + (lane >> 3));
-        if (wid < 2) {
-            const int r = 8 * wid + (lane >> 3);
-            const int g = r < a_rows ? r : a_rows - 1;
-            t.offx = (uint32_t)g * (uint32_t)K + (uint32_t)((c ^ perm8(r)) << 4);
-        } else if (wid == 2) {
-            const int r = lane < a_rows ? lane : a_rows - 1;
-            t.offx = act_quant == MOE_ACT_PER_TENSOR ? 0u : (uint32_t)(tc.row0 + r) * 4u;
-        } else {
-            const int n = lane < b_rows ? lane : b_rows - 1;
-            t.offx = w_quant == MOE_W_PER_EXPERT ? (uint32_t)tc.e * 4u
-                                                 : (uint32_t)((int64_t)tc.e * N + tc.n0 + n) * 4u;
-        }
+        const int c = lane & 7, r0 = lane >> 3, r1 = 8 + (lane >> 3);
+        t.offb0 = (uint32_t)r0 * (uint32_t)K + (uint32_t)((c ^ perm8(r0)) << 4);
+        t.offb1 = (uint32_t)r1 * (uint32_t)K + (uint32_t)((c ^ perm8(r1)) << 4);
+        t.offa0 = (uint32_t)(r0 < a_rows ? r0 : a_rows - 1) * (uint32_t)K + (uint32_t)((c ^ perm8(r0)) << 4);
+        t.offa1 = (uint32_t)(r1 < a_rows ? r1 : a_rows - 1) * (uint32_t)K + (uint32_t)((c ^ perm8(r1)) << 4);
+        const int l = lane & 15;
+        t.offsa = act_quant == MOE_ACT_PER_TENSOR ? 0u : (uint32_t)(tc.row0 + (l < a_rows ? l : a_rows - 1)) * 4u;
+        t.offsb = w_quant == MOE_W_PER_EXPERT ? (uint32_t)tc.e * 4u
+                                              : (uint32_t)((int64_t)tc.e * N + tc.n0 + l) * 4u;
         return t;
     };
     // issue step k of unit u (descriptor t) into stage s
+    const uint8_t* sa_b = uniform_ptr((const uint8_t*)sa);
+    const uint8_t* sb_b = uniform_ptr((const uint8_t*)sb);
     auto issue = [&](const SUnit& t, int u, int k, int s) {
         const uint32_t st = lds0 + (uint32_t)(s * kSStage);
         const uint8_t* bb = uniform_ptr(t.b_g + k * 128);
-        const uint32_t lb = __builtin_amdgcn_readfirstlane(st + wid * 2048);
-        dma16_nt(bb, t.offb0, lb);
-        dma16_nt(bb, t.offb1, lb + 1024);
-        if (wid < 2) {
-            dma16(uniform_ptr(t.a_g + k * 128), t.offx,
-                  __builtin_amdgcn_readfirstlane(st + kSStageB + wid * 1024));
+        const uint8_t* ab = uniform_ptr(t.a_g + k * 128);
+        if (t.shared_b) {  // read again by the expert's other row blocks: keep in L2
+            dma16(bb, t.offb0, __builtin_amdgcn_readfirstlane(st));
+            dma16(bb, t.offb1, __builtin_amdgcn_readfirstlane(st + 1024));
         } else {
-            const uint8_t* base = (const uint8_t*)(wid == 2 ? sa : sb);
-            dma4(uniform_ptr(base), t.offx,
-                 __builtin_amdgcn_readfirstlane(lds_sc + (uint32_t)(((u & 1) * 2 * SC + (wid - 2) * SC) * 4)));
+            dma16_nt(bb, t.offb0, __builtin_amdgcn_readfirstlane(st));
+            dma16_nt(bb, t.offb1, __builtin_amdgcn_readfirstlane(st + 1024));
         }
+        dma16(ab, t.offa0, __builtin_amdgcn_readfirstlane(st + kSStageB));
+        dma16(ab, t.offa1, __builtin_amdgcn_readfirstlane(st + kSStageB + 1024));
+        const uint32_t sc = lds_sc + (uint32_t)((u & 1) * 128 * 4);
+        dma4(sa_b, t.offsa, __builtin_amdgcn_readfirstlane(sc));
+        dma4(sb_b, t.offsb, __builtin_amdgcn_readfirstlane(sc + 64 * 4));
     };
 
-    // issue cursor: step ji of unit ui (descriptor ti), SSTAGES - 1 steps ahead
+    // issue cursor (unit ui, step ki; ji steps issued so far) runs SSTAGES - 1 ahead
     int ui = 0, ki = 0, ji = 0;
     SUnit ti = setup(0);
     SUnit tc = ti;  // unit being consumed
@@ -1291,32 +1287,31 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
     int uc = 0, kc = 0;
     for (int j = 0; j < n_steps; ++j) {
-        // this wave's loads of step j are done once at most the later issued steps remain
-        const int later = ji - 1 - j;
-        wait_steps(later);
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
-        __syncthreads();  // step j complete in LDS; stage (j - 1) % SSTAGES is free
+        // step j's loads are done once at most the later issued steps remain
+        wait_steps(ji - 1 - j);
+        // lgkmcnt(0): the reads of step j - 1, whose stage the next issue fills, are done
+        __builtin_amdgcn_s_waitcnt(0xC07F);
         if (ji < n_steps) {
             issue(ti, ui, ki, ji % SSTAGES);
             ++ji;
             if (++ki == nk) { ki = 0; if (++ui < n_units) ti = setup(ui); }
         }
-        const uint8_t* st = lds + (j % SSTAGES) * kSStage;
-        const v8i bo = lds_operand(st + wid * 2048, lane & 15, lane);
+        const uint8_t* st = &lds[wid][(j % SSTAGES) * kSStage];
+        const v8i bo = lds_operand(st, lane & 15, lane);
         const v8i ao = lds_operand(st + kSStageB, lane & 15, lane);
         acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bo, ao, acc, 0, 0, 0, 0, 0, 0);
         if (++kc == nk) {
-            // epilogue: lane l, value v = row row0 + l % 16, column n0 + 16 w + 4 (l / 16) + v
-            const float* sc = &s_scale[uc & 1][0];
+            // lane l, value v: row row0 + l % 16, column n0 + 4 (l / 16) + v
+            const float* sc = &s_scale[wid][uc & 1][0];
             const int m = tc.row0 + (lane & 15);
-            const int nl = 16 * wid + 4 * (lane >> 4);
-            const int n = tc.n0 + nl;
+            const int nl = 4 * (lane >> 4);
             const float srow = sc[lane & 15];
             float hv[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) hv[v] = acc[v] * (srow * sc[SC + nl + v]);
-            if (m < tc.row_end && n < N)
-                *(uint2*)(C + (int64_t)m * N + n) = make_uint2(bf16x2_rne(hv[0], hv[1]), bf16x2_rne(hv[2], hv[3]));
+            for (int v = 0; v < 4; ++v) hv[v] = acc[v] * (srow * sc[64 + nl + v]);
+            if (m < tc.row_end)
+                *(uint2*)(C + (int64_t)m * N + tc.n0 + nl) =
+                    make_uint2(bf16x2_rne(hv[0], hv[1]), bf16x2_rne(hv[2], hv[3]));
             acc = v4f{0.f, 0.f, 0.f, 0.f};
             kc = 0;
             if (++uc < n_units) tc = setup(uc);
@@ -1353,12 +1348,12 @@ extern "C" int moe_grouped_gemm_fp8(const uint8_t* a_q, const float* a_scale, in
     (void)hipGetLastError();
     const bool kdep_modes = act_quant == MOE_ACT_PER_GROUP || w_quant == MOE_W_BLOCK;
     if (!kdep_modes && K % 128 == 0 && K / 128 >= SSTAGES && m_cap <= (int64_t)64 * num_local &&
-        (int64_t)K * SC < ((int64_t)1 << 32) && (int64_t)num_local * N * 4 < ((int64_t)1 << 32)) {
+        (int64_t)K * SM < ((int64_t)1 << 32) && (int64_t)num_local * N * 4 < ((int64_t)1 << 32)) {
         // few rows per expert (at most 64 on average even if every row slot is
         // filled): stream each expert's weights once
-        const int64_t upper = (ceil_div(m_cap, SM) + num_local) * ceil_div(N, SC);
+        const int64_t upper = (ceil_div(m_cap, SM) + num_local) * ceil_div(N, SC);  // units
         int64_t g = 2 * (int64_t)device_cu_count();
-        if (g > ceil_div(upper, 8) * 8) g = ceil_div(upper, 8) * 8;
+        if (g > ceil_div(upper, 32) * 8) g = ceil_div(upper, 32) * 8;  // four waves per block
         g = ceil_div(g < 8 ? 8 : g, 8) * 8;
         hipLaunchKernelGGL(grouped_gemm_stream_kernel, dim3((unsigned)g), dim3(256), 0, (hipStream_t)stream,
                            a_q, a_scale, act_quant, b_q, b_scale, w_quant, seg_indptr, num_local, m_cap, N, K,

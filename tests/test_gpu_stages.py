@@ -298,9 +298,10 @@ def test_grouped_gemm_random_256_tiles(act_quant, w_quant, N, K):
 
 # Cases with m_cap at most 64 rows per local expert, K a multiple of 1024 and no
 # K-dependent scale, where the library streams each expert's weights once (one
-# block per expert and 64-column slice, 16 rows of the expert per pass): one-pass
-# segments (1, 2, 3, 5, 16 rows), two- and three-pass ones (17, 33, 48), empty
-# experts, and column counts that leave a partial 64-column slice.
+# wave per unit of 16 rows x 16 columns of an expert): one-unit-high segments
+# (1, 2, 3, 5, 16 rows), two- and three-unit ones (17, 33, 48), whose weights
+# the units share through L2, empty experts, and column counts that are not a
+# multiple of 64.
 SMALL_COUNTS = (3, 0, 17, 33, 1, 16, 0, 48, 5, 2)
 PLAIN_MODES = [(W.ACT_PER_TENSOR, W.W_PER_EXPERT), (W.ACT_PER_TOKEN, W.W_PER_EXPERT),
                (W.ACT_PER_TOKEN, W.W_PER_CHANNEL), (W.ACT_PER_TENSOR, W.W_PER_CHANNEL)]
