@@ -9,9 +9,10 @@
 // registers between the amax and the encode for rows up to 8192 wide; all of
 // a row's loads are issued before the first is used). The
 // per-tensor mode needs the maximum over all M*I values first: pass 1 writes a
-// partial maximum per block, pass 2 reduces the partials in every block and
-// recomputes h while encoding (re-reading gate/up costs the same bytes as
-// storing and re-reading h).
+// partial maximum per block, evaluating SiLU only for values whose cheap upper
+// bound could raise the maximum; pass 2 reduces the partials in every block and
+// computes h while encoding (re-reading gate/up costs the same bytes as storing
+// and re-reading h).
 #include "common.h"
 
 namespace moe {
@@ -190,7 +191,15 @@ __global__ __launch_bounds__(256) void act_requant_wide_kernel(const uint16_t* _
     }
 }
 
-// per tensor, pass 1: partial maxima of |h|
+// per tensor, pass 1: partial maxima of |h|, with SiLU evaluated only where it
+// can matter. For every value, |h| = |bf16(silu(g) * u)| <= max(g, 0.28) * |u|
+// * (1 + 2^-7): silu(g) = g / (1 + exp(-g)) divides by at least 1, so it never
+// exceeds g, and for g < 0 its magnitude stays below 0.2785; the fp32 product
+// and the bf16 rounding add less than 2^-7. A group of 1024 values (16 per lane)
+// is evaluated exactly only if some value's bound times 1.01 reaches the wave's
+// running maximum of exact |h| values; otherwise none of them can raise it. The
+// value that attains the maximum is always evaluated exactly, so the result is
+// the same maximum as evaluating every value (fmaxf ignores NaN either way).
 __global__ __launch_bounds__(256) void act_amax_kernel(const uint16_t* __restrict__ gu,
                                                        const int32_t* __restrict__ seg, int num_local,
                                                        int64_t m_cap, int I, float* __restrict__ part) {
@@ -198,14 +207,25 @@ __global__ __launch_bounds__(256) void act_amax_kernel(const uint16_t* __restric
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t M = rows_present(seg, num_local, m_cap);
     const int nit = (I + 1023) / 1024;
-    float amax = 0.0f;
+    float amax = 0.0f;  // wave-uniform: maximum of the exact |h| seen so far
     for (int64_t row = (int64_t)blockIdx.x * 4 + wid; row < M; row += (int64_t)gridDim.x * 4)
         for (int it = 0; it < nit; ++it) {
+            const int c = it * 1024 + lane * 16;
+            const GU16 v = load_gu16(gu, row, I, c);
+            const uint32_t g[8] = {v.ga.x, v.ga.y, v.ga.z, v.ga.w, v.gb.x, v.gb.y, v.gb.z, v.gb.w};
+            const uint32_t u[8] = {v.ua.x, v.ua.y, v.ua.z, v.ua.w, v.ub.x, v.ub.y, v.ub.z, v.ub.w};
+            float bound = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                bound = fmaxf(bound, fmaxf(bf16_lo(g[q]), 0.28f) * fabsf(bf16_lo(u[q])));
+                bound = fmaxf(bound, fmaxf(bf16_hi(g[q]), 0.28f) * fabsf(bf16_hi(u[q])));
+            }
+            const bool cand = c < I && !(bound * 1.01f < amax);  // NaN bounds count as candidates
+            if (__builtin_amdgcn_ballot_w64(cand) == 0) continue;
             uint4 h0, h1;
-            silu_mul16(gu, row, I, it * 1024 + lane * 16, h0, h1);
-            amax = fmaxf(amax, amax16(h0, h1));
+            silu_mul16_from(v, I, c, h0, h1);
+            amax = wave_max(fmaxf(amax, amax16(h0, h1)));
         }
-    amax = wave_max(amax);
     if (lane == 0) red[wid] = amax;
     __syncthreads();
     if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
