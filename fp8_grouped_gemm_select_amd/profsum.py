@@ -210,6 +210,26 @@ def stats_md(path):
     return "\n".join(lines) + "\n"
 
 
+def bench_md(path):
+    """The benchmark line the profiled command printed (its last JSON line):
+    headline figures, the roofline object and the on-box ceilings, if any."""
+    line = None
+    with open(path) as f:
+        for raw in f:
+            raw = raw.strip()
+            if raw.startswith("{") and raw.endswith("}"):
+                line = raw
+    if line is None:
+        return ""
+    d = json.loads(line)
+    lines = ["", "Benchmark line of the same run (under the profiler, so slower than an unprofiled run):", "",
+             f"- {d.get('metric')}: {d.get('value')} {d.get('unit')}, {d.get('ms_per_step')} ms per step",
+             f"- roofline: `{json.dumps(d.get('roofline'))}`"]
+    if d.get("ceilings"):
+        lines.append(f"- on-box ceilings: `{json.dumps(d['ceilings'])}`")
+    return "\n".join(lines) + "\n"
+
+
 def _per_pass_sums(ds, stage, key="dur_us"):
     """Sum `key` over the kernels of a multi-kernel stage within each layer pass
     (a pass starts at every select_experts dispatch)."""
@@ -294,6 +314,7 @@ def main(argv=None):
     a.add_argument("--command", required=True)
     a.add_argument("--out", required=True)
     a.add_argument("--stats", help="the run's --stats kernel summary CSV, appended as a table")
+    a.add_argument("--bench-log", help="the profiled benchmark's output; its JSON line is appended")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -317,6 +338,8 @@ def main(argv=None):
             f.write(trace_md(args.csv, args.workload, args.command))
             if args.stats:
                 f.write(stats_md(args.stats))
+            if args.bench_log:
+                f.write(bench_md(args.bench_log))
     else:
         t = traffic(args.fetch_csv, args.write_csv, args.calib_bytes, args.workload, args.command)
         with open(args.out_json, "w") as f:
