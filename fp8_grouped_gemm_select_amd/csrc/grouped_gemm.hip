@@ -868,14 +868,22 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_256_kernel(
                             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                 bfr[j], af, acc[i][j], 0, 0, 0, 0, 0, 0);
                     } else {
+                        // each MFMA starts from zero and is added with the step's factor; two
+                        // results in flight, so MFMA j + 1 runs while result j is added
                         const float f = (group_act ? s_sa[s][rb * 16 + (lane & 15)] : 1.0f) * sbv;
+                        const v4f z = v4f{0.f, 0.f, 0.f, 0.f};
+                        v4f t0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[0], af, z, 0, 0, 0, 0, 0, 0);
+                        v4f t1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[1], af, z, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                bfr[j], af, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                        for (int v = 0; v < 4; ++v) acc[i][0][v] = __builtin_fmaf(t0[v], f, acc[i][0][v]);
+                        t0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[2], af, z, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-                            for (int v = 0; v < 4; ++v) acc[i][j][v] = acc[i][j][v] + t[v] * f;
-                        }
+                        for (int v = 0; v < 4; ++v) acc[i][1][v] = __builtin_fmaf(t1[v], f, acc[i][1][v]);
+                        t1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bfr[3], af, z, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[i][2][v] = __builtin_fmaf(t0[v], f, acc[i][2][v]);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[i][3][v] = __builtin_fmaf(t1[v], f, acc[i][3][v]);
                     }
                     af = an;
                 }
