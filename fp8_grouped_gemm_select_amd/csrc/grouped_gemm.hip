@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void grouped_gemm_kernel(
                         const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             bfr[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) acc[i][j][v] = acc[i][j][v] + t[v] * f;
+                        for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(t[v], f, acc[i][j][v]);
                     }
                 }
             }
@@ -647,7 +647,7 @@ __global__ __launch_bounds__(kDThreads, 1) void grouped_gemm_dma_kernel(
                                 const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                     bfr[j], af[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-                                for (int v = 0; v < 4; ++v) acc[i][j][v] = acc[i][j][v] + t[v] * f;
+                                for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(t[v], f, acc[i][j][v]);
                             }
                         }
                     }
