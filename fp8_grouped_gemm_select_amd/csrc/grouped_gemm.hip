@@ -1328,6 +1328,177 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(
     wait_vmcnt<0>();
 }
 
+// ---- few rows per expert, MXFP4 weights: weight streaming ----
+//
+// The scheme of the FP8 streaming kernel with 256-deep K steps, so that a weight
+// row's step is one 128-byte line (256 E2M1 codes) as in the FP8 kernel: per
+// step a wave's stage holds its 16 weight rows (2 KB, perm8 layout), their
+// eight E8M0 block scales each (one 4-byte DMA: lane l brings dword l % 2 of
+// row (l % 32) / 2), and the unit's activation rows of 256 bytes (chunk c of row
+// r at c ^ r), and two 128-deep scaled MFMAs consume it with the operand orders
+// of the tiled FP4 kernel. A unit has 8 rows here (an 8 x 256-byte activation
+// stage), so that four stages per wave fit two blocks per CU; the MFMA's lanes
+// for rows 8-15 read rows 0-7 again and those outputs are not stored. Seven DMA
+// instructions per step: weights (two), their scales (one), activations (two),
+// the unit's fp32 row and column scales (one each, into the buffer of the
+// unit's parity).
+constexpr int S4K = 256;
+constexpr int S4M = 8;                          // rows per unit
+constexpr int S4STAGES = 4;
+constexpr int kS4StageB = SC * 128;             // 2 KB of E2M1 codes
+constexpr int kS4StageS = 256;                  // E8M0 scales (128 bytes used)
+constexpr int kS4StageA = S4M * S4K;            // 2 KB of activations
+constexpr int kS4Stage = kS4StageB + kS4StageS + kS4StageA;
+constexpr int kS4Dma = 7;
+constexpr int kS4MaxLocal = 256;
+
+__device__ __forceinline__ void wait_steps4(int n) {
+    switch (n) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<kS4Dma>(); break;
+        default: wait_vmcnt<2 * kS4Dma>(); break;
+    }
+}
+static_assert(S4STAGES - 2 == 2, "wait_steps4 covers 0 .. S4STAGES - 2 steps");
+
+struct S4Unit {
+    int row0, row_end, n0, shared_b;
+    const uint8_t* a_g;  // first activation row
+    const uint8_t* b_g;  // first weight row (E2M1 codes)
+    const uint8_t* e_g;  // its E8M0 scales
+    uint32_t offb0, offb1, offe, offa0, offa1, offsa, offsb;
+};
+
+__global__ __launch_bounds__(256, 2) void grouped_gemm_stream_fp4_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sa, int act_quant,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Be8, const float* __restrict__ sb, int w_quant,
+    const int32_t* __restrict__ seg_in, int num_local, int64_t m_cap, int N, int K,
+    uint16_t* __restrict__ C) {
+    __shared__ __align__(16) uint8_t lds[4][S4STAGES * kS4Stage];
+    __shared__ __align__(16) float s_scale[4][2][128];
+    __shared__ int s_seg[kS4MaxLocal + 1];
+    __shared__ int s_tstart[kS4MaxLocal + 1];
+    __shared__ int scan_scratch[17];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nk = K / S4K;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const void*)&lds[wid][0];
+    const uint32_t lds_sc = (uint32_t)(uintptr_t)(const void*)&s_scale[wid][0][0];
+
+    const int total = build_tile_table<S4M, SC>(seg_in, num_local, m_cap, N, s_seg, s_tstart, scan_scratch);
+    const int xcd = blockIdx.x & 7;
+    const int per_xcd_waves = (gridDim.x >> 3) * 4;
+    const int wx = (blockIdx.x >> 3) * 4 + wid;
+    const int per_xcd = (total + 7) / 8;
+    const int lt_begin = xcd * per_xcd + wx;
+    const int lt_end = xcd * per_xcd + per_xcd < total ? xcd * per_xcd + per_xcd : total;
+    if (lt_begin >= lt_end) return;
+    const int n_units = (lt_end - lt_begin + per_xcd_waves - 1) / per_xcd_waves;
+    const int n_steps = n_units * nk;
+
+    auto setup = [&](int u) {
+        const TileCoord tc = tile_coord<S4M, SC>(lt_begin + u * per_xcd_waves, s_seg, s_tstart, num_local);
+        S4Unit t;
+        t.row0 = tc.row0;
+        t.row_end = tc.row_end;
+        t.n0 = tc.n0;
+        t.shared_b = s_seg[tc.e + 1] - s_seg[tc.e] > S4M;
+        const int a_rows = tc.row_end - tc.row0;
+        t.a_g = A + (int64_t)tc.row0 * K;
+        t.b_g = B + ((int64_t)tc.e * N + tc.n0) * (K / 2);
+        t.e_g = Be8 + ((int64_t)tc.e * N + tc.n0) * (K / 32);
+        // weights: rows 8 i + lane / 8 at chunk position lane % 8 (global chunk
+        // (lane % 8) ^ perm8(row)); their scales: dword lane % 2 of row (lane % 32) / 2
+        const int c8 = lane & 7, r0 = lane >> 3, r1 = 8 + (lane >> 3);
+        t.offb0 = (uint32_t)r0 * (uint32_t)(K / 2) + (uint32_t)((c8 ^ perm8(r0)) << 4);
+        t.offb1 = (uint32_t)r1 * (uint32_t)(K / 2) + (uint32_t)((c8 ^ perm8(r1)) << 4);
+        t.offe = (uint32_t)((lane & 31) >> 1) * (uint32_t)(K / 32) + (uint32_t)((lane & 1) * 4);
+        // activations: rows 4 i + lane / 16 (clamped to the unit's rows) at chunk
+        // position lane % 16 (global chunk (lane % 16) ^ row)
+        const int c16 = lane & 15, q0 = lane >> 4, q1 = 4 + (lane >> 4);
+        t.offa0 = (uint32_t)(q0 < a_rows ? q0 : a_rows - 1) * (uint32_t)K + (uint32_t)((c16 ^ q0) << 4);
+        t.offa1 = (uint32_t)(q1 < a_rows ? q1 : a_rows - 1) * (uint32_t)K + (uint32_t)((c16 ^ q1) << 4);
+        const int l = lane & 15;
+        t.offsa = act_quant == MOE_ACT_PER_TENSOR ? 0u : (uint32_t)(tc.row0 + (l < a_rows ? l : a_rows - 1)) * 4u;
+        t.offsb = w_quant == MOE_W_PER_EXPERT ? (uint32_t)tc.e * 4u
+                                              : (uint32_t)((int64_t)tc.e * N + tc.n0 + l) * 4u;
+        return t;
+    };
+    const uint8_t* sa_b = uniform_ptr((const uint8_t*)sa);
+    const uint8_t* sb_b = uniform_ptr((const uint8_t*)sb);
+    auto issue = [&](const S4Unit& t, int u, int k, int s) {
+        const uint32_t st = lds0 + (uint32_t)(s * kS4Stage);
+        const uint8_t* bb = uniform_ptr(t.b_g + k * (S4K / 2));
+        const uint8_t* eb = uniform_ptr(t.e_g + k * (S4K / 32));
+        const uint8_t* ab = uniform_ptr(t.a_g + k * S4K);
+        if (t.shared_b) {  // read again by the expert's other row blocks: keep in L2
+            dma16(bb, t.offb0, __builtin_amdgcn_readfirstlane(st));
+            dma16(bb, t.offb1, __builtin_amdgcn_readfirstlane(st + 1024));
+        } else {
+            dma16_nt(bb, t.offb0, __builtin_amdgcn_readfirstlane(st));
+            dma16_nt(bb, t.offb1, __builtin_amdgcn_readfirstlane(st + 1024));
+        }
+        dma4(eb, t.offe, __builtin_amdgcn_readfirstlane(st + kS4StageB));
+        dma16(ab, t.offa0, __builtin_amdgcn_readfirstlane(st + kS4StageB + kS4StageS));
+        dma16(ab, t.offa1, __builtin_amdgcn_readfirstlane(st + kS4StageB + kS4StageS + 1024));
+        const uint32_t sc = lds_sc + (uint32_t)((u & 1) * 128 * 4);
+        dma4(sa_b, t.offsa, __builtin_amdgcn_readfirstlane(sc));
+        dma4(sb_b, t.offsb, __builtin_amdgcn_readfirstlane(sc + 64 * 4));
+    };
+
+    int ui = 0, ki = 0, ji = 0;
+    S4Unit ti = setup(0);
+    S4Unit tc = ti;
+    for (; ji < S4STAGES - 1 && ji < n_steps; ++ji) {
+        issue(ti, ui, ki, ji % S4STAGES);
+        if (++ki == nk) { ki = 0; if (++ui < n_units) ti = setup(ui); }
+    }
+    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+    int uc = 0, kc = 0;
+    const int ra = lane & 7;  // activation row of this lane's MFMA operand (rows 8-15 repeat 0-7)
+    for (int j = 0; j < n_steps; ++j) {
+        wait_steps4(ji - 1 - j);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads of step j - 1 are done
+        if (ji < n_steps) {
+            issue(ti, ui, ki, ji % S4STAGES);
+            ++ji;
+            if (++ki == nk) { ki = 0; if (++ui < n_units) ti = setup(ui); }
+        }
+        const uint8_t* lb = &lds[wid][(j % S4STAGES) * kS4Stage];
+        const uint8_t* le = lb + kS4StageB;
+        const uint8_t* la = le + kS4StageS;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // two 128-deep MFMA steps
+            const int rb = lane & 15;
+            const uint4 q = *(const uint4*)(lb + swz(rb, h * 4 + (lane >> 4)));
+            const v8i bo = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+            const int scl = (int)le[rb * 8 + h * 4 + (lane >> 4)];
+            const int c = h * 8 + (lane >> 4);
+            const uint4 lo = *(const uint4*)(la + swz256(ra, c));
+            const uint4 hi = *(const uint4*)(la + swz256(ra, c + 4));
+            const v8i ao = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bo, ao, acc, 4, 0, 0, scl, 0, 127);
+        }
+        if (++kc == nk) {
+            const float* sc = &s_scale[wid][uc & 1][0];
+            const int m = tc.row0 + (lane & 15);
+            const int nl = 4 * (lane >> 4);
+            const float srow = sc[lane & 15];
+            float hv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) hv[v] = acc[v] * (srow * sc[64 + nl + v]);
+            if (m < tc.row_end)
+                *(uint2*)(C + (int64_t)m * N + tc.n0 + nl) =
+                    make_uint2(bf16x2_rne(hv[0], hv[1]), bf16x2_rne(hv[2], hv[3]));
+            acc = v4f{0.f, 0.f, 0.f, 0.f};
+            kc = 0;
+            if (++uc < n_units) tc = setup(uc);
+        }
+    }
+    wait_vmcnt<0>();
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -1439,6 +1610,18 @@ extern "C" int moe_grouped_gemm_mxfp4(const uint8_t* a_q, const float* a_scale, 
         return MOE_ERR_INVALID_ARG;
 
     (void)hipGetLastError();
+    if (K % S4K == 0 && K / S4K >= S4STAGES && m_cap <= (int64_t)64 * num_local && num_local <= kS4MaxLocal &&
+        (int64_t)K * SC < ((int64_t)1 << 32) && (int64_t)num_local * N * (K / 32) < ((int64_t)1 << 32)) {
+        // few rows per expert: stream each expert's weights once
+        const int64_t units = (ceil_div(m_cap, S4M) + num_local) * ceil_div(N, SC);
+        int64_t g = 2 * (int64_t)device_cu_count();
+        if (g > ceil_div(units, 32) * 8) g = ceil_div(units, 32) * 8;  // four waves per block
+        g = ceil_div(g < 8 ? 8 : g, 8) * 8;
+        hipLaunchKernelGGL(grouped_gemm_stream_fp4_kernel, dim3((unsigned)g), dim3(256), 0, (hipStream_t)stream,
+                           a_q, a_scale, act_quant, b_fp4, b_e8m0, b_scale, w_quant, seg_indptr, num_local, m_cap,
+                           N, K, (uint16_t*)c_bf16);
+        return launch_status();
+    }
     const int64_t upper = (ceil_div(m_cap, DBM) + num_local) * ceil_div(N, DBN);
     int64_t g = (int64_t)device_cu_count();
     if (g > ceil_div(upper, 8) * 8) g = ceil_div(upper, 8) * 8;

@@ -96,8 +96,64 @@ def test_mxfp4_gemm_random(act_quant, w_quant, dims):
     print(f"worst |diff| beyond one ulp, relative to sum|products|: {worst:.3g}")
 
 
+# Row capacity of at most 64 rows per local expert with K a multiple of 256 and
+# at least 1024: the weight-streaming kernel (units of 8 rows x 16 columns over
+# 256-deep K steps). Segments of 1-8 rows (one unit high), 9, 17 and 24 (two and
+# three units sharing the expert's weights), empty experts, and column counts
+# that are not a multiple of 64.
+STREAM_COUNTS = (3, 0, 17, 9, 1, 8, 0, 24, 5, 2)
+
+
+@pytest.mark.parametrize("act_quant,w_quant", [(W.ACT_PER_TENSOR, W.W_PER_EXPERT),
+                                               (W.ACT_PER_TOKEN, W.W_PER_CHANNEL),
+                                               (W.ACT_PER_TOKEN, W.W_PER_EXPERT)])
+def test_mxfp4_gemm_exact_case_streaming(act_quant, w_quant):
+    """The exact case of test_mxfp4_gemm_exact_case on the weight-streaming path;
+    bit-identical."""
+    g = np.random.default_rng(13)
+    seg = _seg(STREAM_COUNTS)
+    E, K, N = len(STREAM_COUNTS), 1024, 80
+    m_cap = 64 * E
+    a_q = W.to_e4m3_codes(g.integers(-1, 2, size=(m_cap, K)).astype(np.float32))
+    nib = np.array([0, 1, 2, 4, 9, 10, 12], np.uint8)[g.integers(0, 7, size=(E, N, K))]
+    b_fp4 = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    b_e8m0 = g.integers(126, 128, size=(E, N, K // 32)).astype(np.uint8)
+    sa = np.ldexp(1.0, g.integers(-2, 3, size=1 if act_quant == W.ACT_PER_TENSOR else m_cap)).astype(np.float32)
+    sb = np.ldexp(1.0, g.integers(-2, 3, size=E if w_quant == W.W_PER_EXPERT else E * N)).astype(np.float32)
+    print(f"mxfp4 exact streaming act={act_quant} w={w_quant}", flush=True)
+    ref = oracle.grouped_gemm_mxfp4(a_q, sa, act_quant, b_fp4, b_e8m0, sb, w_quant, seg)
+    c = G.run_gemm_fp4(a_q, sa, act_quant, b_fp4, b_e8m0, sb, w_quant, seg)
+    M = int(seg[-1])
+    assert np.array_equal(c[:M], ref[:M])
+
+
+@pytest.mark.parametrize("act_quant,w_quant", [(W.ACT_PER_TENSOR, W.W_PER_EXPERT),
+                                               (W.ACT_PER_TOKEN, W.W_PER_CHANNEL)])
+@pytest.mark.parametrize("N,K", [(272, 2048), (80, 1024), (1040, 7168)])
+def test_mxfp4_gemm_random_streaming(act_quant, w_quant, N, K):
+    """Random codes and block scales on the weight-streaming path: within one
+    bf16 step plus both sides' summation bounds."""
+    g = np.random.default_rng(17)
+    seg = _seg(STREAM_COUNTS)
+    E = len(STREAM_COUNTS)
+    m_cap = 64 * E
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    a_q = finite[g.integers(0, len(finite), (m_cap, K))]
+    b_fp4, b_e8m0 = _fp4_weights(g, E, N, K)
+    sa = g.uniform(1e-3, 4e-3, 1 if act_quant == W.ACT_PER_TENSOR else m_cap).astype(np.float32)
+    sb = g.uniform(0.5, 2.0, E if w_quant == W.W_PER_EXPERT else E * N).astype(np.float32)
+    print(f"mxfp4 random streaming N={N} K={K} act={act_quant} w={w_quant}", flush=True)
+    ref = oracle.grouped_gemm_mxfp4(a_q, sa, act_quant, b_fp4, b_e8m0, sb, w_quant, seg)
+    c = G.run_gemm_fp4(a_q, sa, act_quant, b_fp4, b_e8m0, sb, w_quant, seg)
+    M = int(seg[-1])
+    rows = np.arange(M)
+    worst = G.assert_sum_close(c[:M], ref[:M], abs_products_fp4(a_q, sa, act_quant, b_fp4, b_e8m0, sb,
+                                                                 w_quant, seg, rows), K, what="C")
+    print(f"worst |diff| beyond one ulp, relative to sum|products|: {worst:.3g}")
+
+
 @pytest.mark.parametrize("name,which", [("dsv3_prefill_ep_fp4", "w13"), ("dsv3_prefill_ep_fp4", "w2"),
-                                        ("dsv3_decode_ep_fp4", "w13")])
+                                        ("dsv3_decode_ep_fp4", "w13"), ("dsv3_decode_ep_fp4", "w2")])
 def test_mxfp4_gemm_full_size_sampled_rows(name, which):
     cfg = W.CONFIGS[name]
     inp = W.gen_layer_inputs(cfg, weights=False)
@@ -116,7 +172,10 @@ def test_mxfp4_gemm_full_size_sampled_rows(name, which):
     b_fp4, b_e8m0, sb = W.gen_weights_fp4(cfg, which)
     print(f"mxfp4 full {name} {which} M={M} N={N} K={K}", flush=True)
     c = G.run_gemm_fp4(a_q, sa, cfg.act_quant, b_fp4, b_e8m0, sb, cfg.w_quant, seg)
-    rows = np.unique(np.concatenate([g.integers(0, M, 44), [0, M - 1], seg[1:-1][:2]]))
+    # random rows plus every non-empty segment's first and last row
+    nonempty = np.nonzero(np.diff(seg) > 0)[0]
+    edges = np.concatenate([seg[nonempty], seg[nonempty + 1] - 1])
+    rows = np.unique(np.concatenate([g.integers(0, M, 44), [0, M - 1], edges]))
     rows = rows[rows < M]
     ref = oracle.grouped_gemm_mxfp4_rows(a_q, sa, cfg.act_quant, b_fp4, b_e8m0, sb, cfg.w_quant, seg, rows)
     G.assert_close_layer(c[rows], ref, what="C rows")
