@@ -239,6 +239,11 @@ def main():
         if f:
             stage_stats[name].update(TFLOPs=round(f / t / 1e12, 1),
                                      mfma_frac=round(f / t / 1e12 / FP8_PEAK_TFLOPS, 4))
+        # the stage's floor (bytes at HBM peak or FLOPs at MFMA peak, whichever is
+        # longer) over its time: for a GEMM, its rate as a fraction of
+        # min(MFMA peak, arithmetic intensity x HBM peak)
+        stage_stats[name]["of_roofline"] = round(max(b / (HBM_PEAK_GBS * 1e9),
+                                                     f / (FP8_PEAK_TFLOPS * 1e12)) / t, 4)
     dom = max(stages, key=lambda n: stage_ms[n])
     db, df = work[dom]["bytes"], work[dom]["flops"]
     dt = stage_ms[dom] * 1e-3
@@ -256,8 +261,11 @@ def main():
     roof["traffic"] = measured_traffic(cfg.name, dom)
     gemm_t = (stage_ms["gemm_w13"] + stage_ms["gemm_w2"]) * 1e-3
     gemm_f = work["gemm_w13"]["flops"] + work["gemm_w2"]["flops"]
+    gemm_floor = sum(max(work[n]["bytes"] / (HBM_PEAK_GBS * 1e9), work[n]["flops"] / (FP8_PEAK_TFLOPS * 1e12))
+                     for n in ("gemm_w13", "gemm_w2"))
     gemm = dict(tflops=round(gemm_f / gemm_t / 1e12, 1),
                 frac_of_fp8_peak=round(gemm_f / gemm_t / 1e12 / FP8_PEAK_TFLOPS, 4),
+                frac_of_roofline=round(gemm_floor / gemm_t, 4),
                 w13_tflops=stage_stats["gemm_w13"].get("TFLOPs"),
                 w2_tflops=stage_stats["gemm_w2"].get("TFLOPs"))
 
