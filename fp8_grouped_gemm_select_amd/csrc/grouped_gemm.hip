@@ -1332,41 +1332,61 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_kernel(
 //
 // The scheme of the FP8 streaming kernel with 256-deep K steps, so that a weight
 // row's step is one 128-byte line (256 E2M1 codes) as in the FP8 kernel: per
-// step a wave's stage holds its 16 weight rows (2 KB, perm8 layout), their
-// eight E8M0 block scales each (one 4-byte DMA: lane l brings dword l % 2 of
-// row (l % 32) / 2), and the unit's activation rows of 256 bytes (chunk c of row
-// r at c ^ r), and two 128-deep scaled MFMAs consume it with the operand orders
-// of the tiled FP4 kernel. A unit has 8 rows here (an 8 x 256-byte activation
-// stage), so that four stages per wave fit two blocks per CU; the MFMA's lanes
-// for rows 8-15 read rows 0-7 again and those outputs are not stored. Seven DMA
-// instructions per step: weights (two), their scales (one), activations (two),
-// the unit's fp32 row and column scales (one each, into the buffer of the
-// unit's parity).
+// step a wave's stage holds its 16 weight rows (2 KB, perm8 layout) and the
+// unit's activation rows of 256 bytes (chunk c of row r at c ^ r), and two
+// 128-deep scaled MFMAs consume it with the operand orders of the tiled FP4
+// kernel. A unit has 8 rows here (an 8 x 256-byte activation stage), so that four
+// stages per wave fit two blocks per CU; the MFMA's lanes for rows 8-15 read
+// rows 0-7 again and those outputs are not stored.
+//
+// The weights' E8M0 block scales (8 bytes per row per step) come eight steps at
+// a time: one 16-byte DMA per lane brings 64 bytes of each of the 16 rows into
+// one of two per-wave buffers (alternating by group of eight steps), issued
+// with the group's first step; per step they would cost as many cache lines
+// as the codes. So the DMA count of a step varies: weights (two) and
+// activations (two), plus one at a group's first step, plus two (the unit's
+// fp32 row and column scales, into the buffer of the unit's parity) at a unit's
+// first step. A step waits until only the DMAs of the steps issued after it
+// are in flight, from the recorded counts of the last two issued steps.
 constexpr int S4K = 256;
 constexpr int S4M = 8;                          // rows per unit
 constexpr int S4STAGES = 4;
+constexpr int S4G = 8;                          // K steps per E8M0 scale group
 constexpr int kS4StageB = SC * 128;             // 2 KB of E2M1 codes
-constexpr int kS4StageS = 256;                  // E8M0 scales (128 bytes used)
 constexpr int kS4StageA = S4M * S4K;            // 2 KB of activations
-constexpr int kS4Stage = kS4StageB + kS4StageS + kS4StageA;
-constexpr int kS4Dma = 7;
+constexpr int kS4Stage = kS4StageB + kS4StageA;
+constexpr int kS4Group = SC * S4G * 8;          // 1 KB of E8M0 scales per group
 constexpr int kS4MaxLocal = 256;
 
-__device__ __forceinline__ void wait_steps4(int n) {
+// vmcnt wait for at most n of this wave's DMA instructions still in flight
+// (n <= 14: the two later issued steps, at most seven each)
+__device__ __forceinline__ void wait_dma4(int n) {
     switch (n) {
         case 0: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<kS4Dma>(); break;
-        default: wait_vmcnt<2 * kS4Dma>(); break;
+        case 1: wait_vmcnt<1>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 9: wait_vmcnt<9>(); break;
+        case 10: wait_vmcnt<10>(); break;
+        case 11: wait_vmcnt<11>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        case 13: wait_vmcnt<13>(); break;
+        default: wait_vmcnt<14>(); break;
     }
 }
-static_assert(S4STAGES - 2 == 2, "wait_steps4 covers 0 .. S4STAGES - 2 steps");
+static_assert(S4STAGES - 2 == 2, "wait_dma4 covers the two later issued steps");
 
 struct S4Unit {
     int row0, row_end, n0, shared_b;
     const uint8_t* a_g;  // first activation row
     const uint8_t* b_g;  // first weight row (E2M1 codes)
     const uint8_t* e_g;  // its E8M0 scales
-    uint32_t offb0, offb1, offe, offa0, offa1, offsa, offsb;
+    uint32_t offb0, offb1, offa0, offa1, offsa, offsb;
 };
 
 __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_fp4_kernel(
@@ -1375,6 +1395,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_fp4_kernel(
     const int32_t* __restrict__ seg_in, int num_local, int64_t m_cap, int N, int K,
     uint16_t* __restrict__ C) {
     __shared__ __align__(16) uint8_t lds[4][S4STAGES * kS4Stage];
+    __shared__ __align__(16) uint8_t s_e8[4][2][kS4Group];
     __shared__ __align__(16) float s_scale[4][2][128];
     __shared__ int s_seg[kS4MaxLocal + 1];
     __shared__ int s_tstart[kS4MaxLocal + 1];
@@ -1384,6 +1405,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_fp4_kernel(
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nk = K / S4K;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const void*)&lds[wid][0];
+    const uint32_t lds_e8 = (uint32_t)(uintptr_t)(const void*)&s_e8[wid][0][0];
     const uint32_t lds_sc = (uint32_t)(uintptr_t)(const void*)&s_scale[wid][0][0];
 
     const int total = build_tile_table<S4M, SC>(seg_in, num_local, m_cap, N, s_seg, s_tstart, scan_scratch);
@@ -1396,6 +1418,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_fp4_kernel(
     if (lt_begin >= lt_end) return;
     const int n_units = (lt_end - lt_begin + per_xcd_waves - 1) / per_xcd_waves;
     const int n_steps = n_units * nk;
+    const int gpu = (nk + S4G - 1) / S4G;  // scale groups per unit
 
     auto setup = [&](int u) {
         const TileCoord tc = tile_coord<S4M, SC>(lt_begin + u * per_xcd_waves, s_seg, s_tstart, num_local);
@@ -1409,11 +1432,10 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_fp4_kernel(
         t.b_g = B + ((int64_t)tc.e * N + tc.n0) * (K / 2);
         t.e_g = Be8 + ((int64_t)tc.e * N + tc.n0) * (K / 32);
         // weights: rows 8 i + lane / 8 at chunk position lane % 8 (global chunk
-        // (lane % 8) ^ perm8(row)); their scales: dword lane % 2 of row (lane % 32) / 2
+        // (lane % 8) ^ perm8(row))
         const int c8 = lane & 7, r0 = lane >> 3, r1 = 8 + (lane >> 3);
         t.offb0 = (uint32_t)r0 * (uint32_t)(K / 2) + (uint32_t)((c8 ^ perm8(r0)) << 4);
         t.offb1 = (uint32_t)r1 * (uint32_t)(K / 2) + (uint32_t)((c8 ^ perm8(r1)) << 4);
-        t.offe = (uint32_t)((lane & 31) >> 1) * (uint32_t)(K / 32) + (uint32_t)((lane & 1) * 4);
         // activations: rows 4 i + lane / 16 (clamped to the unit's rows) at chunk
         // position lane % 16 (global chunk (lane % 16) ^ row)
         const int c16 = lane & 15, q0 = lane >> 4, q1 = 4 + (lane >> 4);
@@ -1427,10 +1449,15 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_fp4_kernel(
     };
     const uint8_t* sa_b = uniform_ptr((const uint8_t*)sa);
     const uint8_t* sb_b = uniform_ptr((const uint8_t*)sb);
-    auto issue = [&](const S4Unit& t, int u, int k, int s) {
+    // lane l of a scale group's DMA: 16 bytes at byte 16 (l % 4) of row l / 4's
+    // 64 (clamped to the row's last 16 bytes past its end; those are not used)
+    const uint32_t e_row = (uint32_t)(lane >> 2) * (uint32_t)(K / 32);
+    // issue step k of unit u (descriptor t) into stage s; gi: the scale groups
+    // issued so far (the buffer of this step's group is (gi - 1) & 1 after a
+    // group start). Returns the number of DMA instructions issued.
+    auto issue = [&](const S4Unit& t, int u, int k, int s, int& gi) {
         const uint32_t st = lds0 + (uint32_t)(s * kS4Stage);
         const uint8_t* bb = uniform_ptr(t.b_g + k * (S4K / 2));
-        const uint8_t* eb = uniform_ptr(t.e_g + k * (S4K / 32));
         const uint8_t* ab = uniform_ptr(t.a_g + k * S4K);
         if (t.shared_b) {  // read again by the expert's other row blocks: keep in L2
             dma16(bb, t.offb0, __builtin_amdgcn_readfirstlane(st));
@@ -1439,41 +1466,59 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_stream_fp4_kernel(
             dma16_nt(bb, t.offb0, __builtin_amdgcn_readfirstlane(st));
             dma16_nt(bb, t.offb1, __builtin_amdgcn_readfirstlane(st + 1024));
         }
-        dma4(eb, t.offe, __builtin_amdgcn_readfirstlane(st + kS4StageB));
-        dma16(ab, t.offa0, __builtin_amdgcn_readfirstlane(st + kS4StageB + kS4StageS));
-        dma16(ab, t.offa1, __builtin_amdgcn_readfirstlane(st + kS4StageB + kS4StageS + 1024));
-        const uint32_t sc = lds_sc + (uint32_t)((u & 1) * 128 * 4);
-        dma4(sa_b, t.offsa, __builtin_amdgcn_readfirstlane(sc));
-        dma4(sb_b, t.offsb, __builtin_amdgcn_readfirstlane(sc + 64 * 4));
+        dma16(ab, t.offa0, __builtin_amdgcn_readfirstlane(st + kS4StageB));
+        dma16(ab, t.offa1, __builtin_amdgcn_readfirstlane(st + kS4StageB + 1024));
+        int n = 4;
+        if (k % S4G == 0) {
+            const int byte = (k / S4G) * (S4G * 8) + (lane & 3) * 16;
+            const int last = K / 32 - 16;
+            dma16(uniform_ptr(t.e_g), e_row + (uint32_t)(byte < last ? byte : last),
+                  __builtin_amdgcn_readfirstlane(lds_e8 + (uint32_t)((gi & 1) * kS4Group)));
+            ++gi;
+            ++n;
+        }
+        if (k == 0) {
+            const uint32_t sc = lds_sc + (uint32_t)((u & 1) * 128 * 4);
+            dma4(sa_b, t.offsa, __builtin_amdgcn_readfirstlane(sc));
+            dma4(sb_b, t.offsb, __builtin_amdgcn_readfirstlane(sc + 64 * 4));
+            n += 2;
+        }
+        return n;
     };
 
-    int ui = 0, ki = 0, ji = 0;
+    // issue cursor: unit ui, step ki, ji steps and gi scale groups issued;
+    // n_last / n_prev: DMA instructions of the last / the one before last issued step
+    int ui = 0, ki = 0, ji = 0, gi = 0, n_last = 0, n_prev = 0;
     S4Unit ti = setup(0);
     S4Unit tc = ti;
     for (; ji < S4STAGES - 1 && ji < n_steps; ++ji) {
-        issue(ti, ui, ki, ji % S4STAGES);
+        n_prev = n_last;
+        n_last = issue(ti, ui, ki, ji % S4STAGES, gi);
         if (++ki == nk) { ki = 0; if (++ui < n_units) ti = setup(ui); }
     }
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
     int uc = 0, kc = 0;
     const int ra = lane & 7;  // activation row of this lane's MFMA operand (rows 8-15 repeat 0-7)
     for (int j = 0; j < n_steps; ++j) {
-        wait_steps4(ji - 1 - j);
+        const int later = ji - 1 - j;
+        wait_dma4(later >= 2 ? n_last + n_prev : (later == 1 ? n_last : 0));
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the reads of step j - 1 are done
         if (ji < n_steps) {
-            issue(ti, ui, ki, ji % S4STAGES);
+            n_prev = n_last;
+            n_last = issue(ti, ui, ki, ji % S4STAGES, gi);
             ++ji;
             if (++ki == nk) { ki = 0; if (++ui < n_units) ti = setup(ui); }
         }
         const uint8_t* lb = &lds[wid][(j % S4STAGES) * kS4Stage];
-        const uint8_t* le = lb + kS4StageB;
-        const uint8_t* la = le + kS4StageS;
+        const uint8_t* la = lb + kS4StageB;
+        // this step's scale group: the (uc * gpu + kc / S4G)-th of this wave
+        const uint8_t* le = &s_e8[wid][(uc * gpu + kc / S4G) & 1][(kc % S4G) * 8];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {  // two 128-deep MFMA steps
             const int rb = lane & 15;
             const uint4 q = *(const uint4*)(lb + swz(rb, h * 4 + (lane >> 4)));
             const v8i bo = v8i{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-            const int scl = (int)le[rb * 8 + h * 4 + (lane >> 4)];
+            const int scl = (int)le[rb * (S4G * 8) + h * 4 + (lane >> 4)];
             const int c = h * 8 + (lane >> 4);
             const uint4 lo = *(const uint4*)(la + swz256(ra, c));
             const uint4 hi = *(const uint4*)(la + swz256(ra, c + 4));
@@ -1610,7 +1655,12 @@ extern "C" int moe_grouped_gemm_mxfp4(const uint8_t* a_q, const float* a_scale, 
         return MOE_ERR_INVALID_ARG;
 
     (void)hipGetLastError();
-    if (K % S4K == 0 && K / S4K >= S4STAGES && m_cap <= (int64_t)64 * num_local && num_local <= kS4MaxLocal &&
+    // (the scale groups of eight steps: every group, a unit's last included, has
+    // at least three steps, so a group's buffer is refilled only after its last
+    // step has been read)
+    const int s4_tail = (K / S4K) % S4G;
+    if (K % 512 == 0 && K / S4K >= S4STAGES && (s4_tail == 0 || s4_tail >= 3) && ((uintptr_t)b_e8m0 & 15u) == 0 &&
+        m_cap <= (int64_t)64 * num_local && num_local <= kS4MaxLocal &&
         (int64_t)K * SC < ((int64_t)1 << 32) && (int64_t)num_local * N * (K / 32) < ((int64_t)1 << 32)) {
         // few rows per expert: stream each expert's weights once
         const int64_t units = (ceil_div(m_cap, S4M) + num_local) * ceil_div(N, SC);

@@ -129,10 +129,11 @@ def test_mxfp4_gemm_exact_case_streaming(act_quant, w_quant):
 
 @pytest.mark.parametrize("act_quant,w_quant", [(W.ACT_PER_TENSOR, W.W_PER_EXPERT),
                                                (W.ACT_PER_TOKEN, W.W_PER_CHANNEL)])
-@pytest.mark.parametrize("N,K", [(272, 2048), (80, 1024), (1040, 7168)])
+@pytest.mark.parametrize("N,K", [(272, 2048), (80, 1024), (1040, 7168), (96, 3584), (64, 2560)])
 def test_mxfp4_gemm_random_streaming(act_quant, w_quant, N, K):
-    """Random codes and block scales on the weight-streaming path: within one
-    bf16 step plus both sides' summation bounds."""
+    """Random codes and block scales on the weight-streaming path (K = 2560, whose
+    last group of eight 256-deep steps would have two, takes the tiled kernel):
+    within one bf16 step plus both sides' summation bounds."""
     g = np.random.default_rng(17)
     seg = _seg(STREAM_COUNTS)
     E = len(STREAM_COUNTS)
