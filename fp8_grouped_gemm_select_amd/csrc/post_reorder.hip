@@ -11,7 +11,7 @@
 namespace moe {
 namespace {
 
-// topk <= 8: the token's local slots are compacted in slot order (n of them,
+// topk <= 8 (or 16): the token's local slots are compacted in slot order (n of them,
 // wave-uniform); each lane covers 16 columns (32 bytes) per iteration and the
 // loads of U iterations of all n slots are issued together, then accumulated
 // in slot order (the same fp32 order as the general kernel below). Fewer local
@@ -66,12 +66,16 @@ __device__ __forceinline__ void combine_token(const uint16_t* __restrict__ down,
     }
 }
 
+// KMAX = 8 (topk <= 8) or 16 (topk <= 16, e.g. eight routed slots and a shared
+// expert's); the 16-slot instance adds a path for 9-16 local slots and is a
+// separate kernel, so that its registers do not lower the 8-slot one's occupancy.
+template <int KMAX>
 __global__ __launch_bounds__(256) void post_reorder8_kernel(const uint16_t* __restrict__ down,
                                                             const int32_t* __restrict__ src2dst,
                                                             const float* __restrict__ w, int64_t T,
                                                             int H, int topk, int64_t m_cap,
                                                             uint16_t* __restrict__ out) {
-    constexpr int K8 = 8;
+    constexpr int K8 = KMAX;
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + wid;
     if (t >= T) return;
@@ -105,6 +109,15 @@ __global__ __launch_bounds__(256) void post_reorder8_kernel(const uint16_t* __re
         const int r4[4] = {rows[0], rows[1], rows[2], rows[3]};
         const float w4[4] = {wj[0], wj[1], wj[2], wj[3]};
         combine_token<4, 2>(down, r4, w4, n, H, lane, orow);
+    } else if (KMAX == 8 || n <= 8) {
+        int r8[8];
+        float w8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            r8[q] = rows[q];
+            w8[q] = wj[q];
+        }
+        combine_token<8, 1>(down, r8, w8, n, H, lane, orow);
     } else {
         combine_token<K8, 1>(down, rows, wj, n, H, lane, orow);
     }
@@ -168,7 +181,11 @@ extern "C" int moe_post_reorder(const void* down_bf16, const int32_t* src2dst,
     if ((down_bf16 && !aligned16(down_bf16)) || !aligned16(out_bf16)) return MOE_ERR_INVALID_ARG;
     (void)hipGetLastError();
     if (topk <= 8)
-        hipLaunchKernelGGL(post_reorder8_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
+        hipLaunchKernelGGL(post_reorder8_kernel<8>, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
+                           (hipStream_t)stream, (const uint16_t*)down_bf16, src2dst, topk_weights, T,
+                           H, topk, m_cap, (uint16_t*)out_bf16);
+    else if (topk <= 16)
+        hipLaunchKernelGGL(post_reorder8_kernel<16>, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
                            (hipStream_t)stream, (const uint16_t*)down_bf16, src2dst, topk_weights, T,
                            H, topk, m_cap, (uint16_t*)out_bf16);
     else

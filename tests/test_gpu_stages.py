@@ -564,16 +564,19 @@ def test_post_reorder(name):
     assert np.all(out[none] == 0)
 
 
-def test_post_reorder_many_slots():
-    """topk above 8 takes the general combine kernel: random local slots, some
-    slots non-local (-1), H not a multiple of the 1024-column step."""
+@pytest.mark.parametrize("topk", [12, 20])
+def test_post_reorder_many_slots(topk):
+    """topk above 8: up to 16 slots take the 16-slot compacting kernel, more the
+    general one; random local slots, some slots non-local (-1), H not a multiple
+    of the 1024-column step."""
     g = np.random.default_rng(6)
-    T, topk, H, m_cap = 37, 12, 144, 37 * 12
+    T, H = 37, 144
+    m_cap = T * topk
     perm = g.permutation(m_cap).astype(np.int32)
     s2d = np.where(g.random(T * topk) < 0.3, -1, perm).astype(np.int32)
     w = g.uniform(0.0, 1.0, (T, topk)).astype(np.float32)
     down = W.to_bf16_bits(g.standard_normal((m_cap, H), dtype=np.float32))
-    print(f"post_reorder general kernel T={T} topk={topk} H={H}", flush=True)
+    print(f"post_reorder many slots T={T} topk={topk} H={H}", flush=True)
     ref = oracle.post_reorder(down, s2d, w, T, topk)
     out = G.run_post(down, s2d, w, T, topk)
     d = np.abs(G.bf16_to_f64(down))
