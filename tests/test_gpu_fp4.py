@@ -153,6 +153,53 @@ def test_mxfp4_gemm_random_streaming(act_quant, w_quant, N, K):
     print(f"worst |diff| beyond one ulp, relative to sum|products|: {worst:.3g}")
 
 
+# One case per FP4 GEMM kernel the library picks: (modes, local experts, m_cap, N, K).
+FP4_PATHS = {
+    "streaming": (W.ACT_PER_TENSOR, W.W_PER_EXPERT, 10, 320, 80, 1024),  # at most 64 rows per expert
+    "tiles256k": (W.ACT_PER_TOKEN, W.W_PER_CHANNEL, 3, 300, 256, 512),   # 256-deep K steps
+    "tiles128k": (W.ACT_PER_TOKEN, W.W_PER_EXPERT, 3, 300, 256, 384),    # K not a multiple of 256
+}
+
+
+def _fp4_case(seed, path):
+    act_quant, w_quant, E, m_cap, N, K = FP4_PATHS[path]
+    g = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    a_q = finite[g.integers(0, len(finite), (m_cap, K))]
+    b_fp4, b_e8m0 = _fp4_weights(g, E, N, K)
+    sa = g.uniform(1e-3, 4e-3, 1 if act_quant == W.ACT_PER_TENSOR else m_cap).astype(np.float32)
+    sb = g.uniform(0.5, 2.0, E if w_quant == W.W_PER_EXPERT else E * N).astype(np.float32)
+    return act_quant, w_quant, a_q, sa, b_fp4, b_e8m0, sb
+
+
+@pytest.mark.parametrize("path", list(FP4_PATHS))
+def test_mxfp4_gemm_all_segments_empty(path):
+    """Every segment empty (M = 0): no row of C is written."""
+    act_quant, w_quant, a_q, sa, b_fp4, b_e8m0, sb = _fp4_case(3, path)
+    seg = np.zeros(b_fp4.shape[0] + 1, np.int32)
+    print(f"mxfp4 all empty {path} m_cap={a_q.shape[0]} N={b_fp4.shape[1]} K={a_q.shape[1]}", flush=True)
+    c = G.run_gemm_fp4(a_q, sa, act_quant, b_fp4, b_e8m0, sb, w_quant, seg)
+    assert np.isnan(G.bf16_to_f64(c)).all(), "a row of C was written although every segment is empty"
+
+
+@pytest.mark.parametrize("path", list(FP4_PATHS))
+def test_mxfp4_gemm_seg_clamped(path):
+    """seg_indptr values outside [0, m_cap] are clamped before use; compared with
+    the oracle on the clamped offsets (every row of C is then written)."""
+    act_quant, w_quant, a_q, sa, b_fp4, b_e8m0, sb = _fp4_case(4, path)
+    E, m_cap, K = b_fp4.shape[0], a_q.shape[0], a_q.shape[1]
+    seg = np.array([-5] + [7] * (E - 1) + [m_cap + 50], np.int32)
+    seg_c = np.clip(seg, 0, m_cap).astype(np.int32)
+    print(f"mxfp4 clamped seg {path} seg={seg.tolist()}", flush=True)
+    ref = oracle.grouped_gemm_mxfp4(a_q, sa, act_quant, b_fp4, b_e8m0, sb, w_quant, seg_c)
+    c = G.run_gemm_fp4(a_q, sa, act_quant, b_fp4, b_e8m0, sb, w_quant, seg)
+    # random codes cancel in places, so the bound is the summation error of both
+    # sides (as in the other random-code cases), not a relative tolerance
+    worst = G.assert_sum_close(c, ref, abs_products_fp4(a_q, sa, act_quant, b_fp4, b_e8m0, sb, w_quant, seg_c,
+                                                        np.arange(m_cap)), K, what="C")
+    print(f"worst |diff| beyond one ulp, relative to sum|products|: {worst:.3g}")
+
+
 @pytest.mark.parametrize("name,which", [("dsv3_prefill_ep_fp4", "w13"), ("dsv3_prefill_ep_fp4", "w2"),
                                         ("dsv3_decode_ep_fp4", "w13"), ("dsv3_decode_ep_fp4", "w2")])
 def test_mxfp4_gemm_full_size_sampled_rows(name, which):

@@ -121,6 +121,64 @@ def test_layer_rsf_scales_output_once():
     assert np.all(np.abs(o25 - 2.5 * o1) <= np.abs(o25) * 2.0 ** -7 + 1e-30)
 
 
+def no_local_inputs(act_quant, w_quant, seed=12):
+    """A layer whose local experts (ids 4-7 of 16) no token selects: their router
+    logits sit far below the rest, so M = 0 on this GPU."""
+    cfg = W.MoEConfig(name="no_local", T=33, H=256, I=128, E=16, topk=2, num_local=4, expert_start=4,
+                      score_fn=W.SCORE_SOFTMAX, act_quant=act_quant, w_quant=w_quant)
+    inp = W.gen_layer_inputs(cfg, seed=seed)
+    logits = inp.logits.copy()
+    logits[:, 4:8] = -60.0
+    return dataclasses.replace(inp, logits=logits)
+
+
+@pytest.mark.parametrize("act_quant,w_quant", [(W.ACT_PER_TENSOR, W.W_PER_EXPERT),
+                                               (W.ACT_PER_GROUP, W.W_BLOCK)])
+def test_layer_no_local_pair(act_quant, w_quant):
+    """Every stage with no local row: seg_indptr all zeros, src2dst all -1 and
+    the output all zeros, as the oracle has it."""
+    inp = no_local_inputs(act_quant, w_quant)
+    ref = oracle.layer(inp)
+    assert int(ref["seg_indptr"][-1]) == 0
+    print(f"layer no local pair act={act_quant} w={w_quant}", flush=True)
+    buf = run_layer(inp)
+    assert np.array_equal(buf.topk_ids.cpu().numpy(), ref["ids"])
+    assert np.array_equal(buf.seg_indptr.cpu().numpy(), ref["seg_indptr"])
+    assert np.all(buf.src2dst.cpu().numpy() == -1)
+    assert np.array_equal(buf.dst2src.cpu().numpy(), ref["dst2src"])
+    out = G.bf16_bits(buf.out)
+    assert np.all(ref["out"] == 0)
+    assert np.array_equal(out, ref["out"])
+
+
+def single_token_cfg(act_quant, w_quant, w_fp4=False):
+    """One token through a DeepSeek-style router (grouped sigmoid with bias,
+    8 of 64 experts) on a 24-expert slice: decode at batch 1."""
+    return W.MoEConfig(name="one_token", T=1, H=512, I=256, E=64, topk=8, num_local=24, expert_start=16,
+                       score_fn=W.SCORE_SIGMOID, n_group=8, topk_group=4, rsf=2.5, use_bias=True,
+                       act_quant=act_quant, w_quant=w_quant, w_fp4=w_fp4)
+
+
+@pytest.mark.parametrize("act_quant,w_quant,w_fp4", [(W.ACT_PER_GROUP, W.W_BLOCK, False),
+                                                     (W.ACT_PER_TOKEN, W.W_PER_CHANNEL, False),
+                                                     (W.ACT_PER_TENSOR, W.W_PER_EXPERT, True)])
+@pytest.mark.parametrize("seed", [14, 8, 0, 30])
+def test_layer_single_token(act_quant, w_quant, w_fp4, seed):
+    """T = 1: ids, permutation and stage-2 codes bit-exact, the output within
+    tolerance. The seeds put 0, 1, 2 and 7 of the token's pairs on the slice."""
+    cfg = single_token_cfg(act_quant, w_quant, w_fp4)
+    inp = W.gen_layer_inputs(cfg, seed=seed)
+    ref = oracle.layer(inp)
+    M = int(ref["seg_indptr"][-1])
+    print(f"layer single token act={act_quant} w={w_quant} fp4={w_fp4} seed={seed} M={M}", flush=True)
+    buf = run_layer(inp)
+    assert np.array_equal(buf.topk_ids.cpu().numpy(), ref["ids"])
+    assert np.array_equal(buf.seg_indptr.cpu().numpy(), ref["seg_indptr"])
+    assert np.array_equal(buf.src2dst.cpu().numpy(), ref["src2dst"])
+    assert np.array_equal(buf.a13.cpu().numpy()[:M], ref["a13"][:M])
+    G.assert_close_layer(G.bf16_bits(buf.out), ref["out"], what="layer output")
+
+
 def e4m3_ordinal(codes):
     """Signed position of an e4m3 code on the number line (codes are sign-magnitude)."""
     c = np.asarray(codes).astype(np.int32)

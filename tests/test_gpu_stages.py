@@ -452,6 +452,51 @@ def test_grouped_gemm_full_size_sampled_rows(name, which):
     print(f"worst |diff| beyond one ulp, relative to sum|products|: {worst:.3g} (2^{np.log2(max(worst, 1e-30)):.1f})")
 
 
+# One case per GEMM kernel the library picks: (modes, local experts, m_cap, N, K).
+GEMM_PATHS = {
+    # no K-dependent scale, K/128 >= 4, at most 64 rows per expert: weight streaming
+    "streaming": (W.ACT_PER_TENSOR, W.W_PER_EXPERT, 10, 320, 80, 1024),
+    # K-dependent scales, at least 128 rows per expert: 256 x 256 tiles
+    "tiles256": (W.ACT_PER_GROUP, W.W_BLOCK, 3, 404, 256, 512),
+    # 128 x 256 tiles, without and with K-dependent scales
+    "tiles128": (W.ACT_PER_TOKEN, W.W_PER_CHANNEL, 4, 400, 256, 512),
+    "tiles128_kdep": (W.ACT_PER_TOKEN, W.W_BLOCK, 4, 400, 256, 512),
+    # K not a multiple of 128: the plain tiled kernel
+    "plain": (W.ACT_PER_TOKEN, W.W_PER_EXPERT, 3, 150, 48, 80),
+}
+
+
+@pytest.mark.parametrize("path", list(GEMM_PATHS))
+def test_grouped_gemm_all_segments_empty(path):
+    """Every segment empty (M = 0, seg_indptr all zeros) with m_cap rows of
+    codes present: no tile exists and no row of C is written."""
+    act_quant, w_quant, E_l, m_cap, N, K = GEMM_PATHS[path]
+    a_q, sa, b_q, sb, _ = _rand_gemm(17, [m_cap] + [0] * (E_l - 1), N, K, act_quant, w_quant, extra=0)
+    seg = np.zeros(E_l + 1, np.int32)
+    print(f"grouped_gemm all empty {path} E_l={E_l} m_cap={m_cap} N={N} K={K}", flush=True)
+    c = G.run_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg)
+    assert np.isnan(G.bf16_to_f64(c)).all(), "a row of C was written although every segment is empty"
+
+
+@pytest.mark.parametrize("path", list(GEMM_PATHS))
+def test_grouped_gemm_seg_clamped(path):
+    """seg_indptr values outside [0, m_cap] are clamped before use: a negative
+    start reads as 0 and a last end past m_cap as m_cap, so the last expert owns
+    every row from its start to m_cap. Compared with the oracle on the clamped
+    offsets."""
+    act_quant, w_quant, E_l, m_cap, N, K = GEMM_PATHS[path]
+    a_q, sa, b_q, sb, _ = _rand_gemm(23, [m_cap] + [0] * (E_l - 1), N, K, act_quant, w_quant, extra=0)
+    mid = 7 if E_l > 2 else m_cap // 3
+    seg = np.array([-5] + [mid] * (E_l - 1) + [m_cap + 50], np.int32)
+    seg_c = np.clip(seg, 0, m_cap).astype(np.int32)
+    print(f"grouped_gemm clamped seg {path} seg={seg.tolist()}", flush=True)
+    ref = oracle.grouped_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg_c)
+    c = G.run_gemm(a_q, sa, act_quant, b_q, sb, w_quant, seg)
+    G.assert_close_layer(c, ref, what="C")
+    G.assert_sum_close(c, ref, abs_products(a_q, sa, act_quant, b_q, sb, w_quant, seg_c, np.arange(m_cap)),
+                       K, what="C")
+
+
 # ---- stage 4 ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("act_quant", [W.ACT_PER_TENSOR, W.ACT_PER_TOKEN, W.ACT_PER_GROUP])
@@ -524,6 +569,37 @@ def test_act_requant_extreme_values(act_quant):
     Gq = 1 if act_quant == W.ACT_PER_TOKEN else -(-I // 128)
     n = 1 if act_quant == W.ACT_PER_TENSOR else M * Gq
     assert np.array_equal(a_s[:n].view(np.uint32), s_ref[:n].view(np.uint32))
+
+
+@pytest.mark.parametrize("act_quant", [W.ACT_PER_TENSOR, W.ACT_PER_TOKEN, W.ACT_PER_GROUP])
+@pytest.mark.parametrize("I", [64, 2048])
+def test_act_requant_no_rows(act_quant, I):
+    """M = 0 (every segment empty) with m_cap rows present: the per-tensor scale
+    is that of an empty maximum (the floored one), bit-exact against the oracle;
+    nothing is written past the outputs."""
+    g = np.random.default_rng(I)
+    m_cap = 21
+    seg = np.zeros(4, np.int32)
+    gu = W.to_bf16_bits((g.standard_normal((m_cap, 2 * I)) * 1.7).astype(np.float32))
+    print(f"act_requant no rows I={I} mode={act_quant}", flush=True)
+    a_ref, s_ref = oracle.act_requant(gu, seg, act_quant)
+    a_q, a_s = G.run_act(gu, seg, act_quant)
+    if act_quant == W.ACT_PER_TENSOR:
+        assert a_s[0].view(np.uint32) == s_ref[0].view(np.uint32)
+
+
+def test_post_reorder_no_local_slot():
+    """No slot of any token is local (src2dst all -1): every output row is zero."""
+    g = np.random.default_rng(8)
+    T, topk, H, m_cap = 9, 8, 7168, 16
+    s2d = np.full(T * topk, -1, np.int32)
+    w = g.uniform(0.0, 1.0, (T, topk)).astype(np.float32)
+    down = W.to_bf16_bits(g.standard_normal((m_cap, H), dtype=np.float32))
+    print(f"post_reorder no local slot T={T} topk={topk} H={H}", flush=True)
+    ref = oracle.post_reorder(down, s2d, w, T, topk)
+    out = G.run_post(down, s2d, w, T, topk)
+    assert np.all(ref == 0)
+    assert np.array_equal(out, ref)
 
 
 @pytest.mark.parametrize("name", ["dsv3_prefill_ep", "mixtral", "skewed_block"])
