@@ -208,6 +208,15 @@ __device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_
                  : "memory");
 }
 
+// A 16-byte store with the nontemporal hint: for output that no later work of the
+// same kernel reads (a GEMM's result rows), so that it does not displace operand
+// lines from L2.
+typedef int moe_i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16_nt(void* p, uint4 v) {
+    const moe_i32x4 w = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    __builtin_nontemporal_store(w, (moe_i32x4*)p);
+}
+
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
     const uint64_t v = (uint64_t)p;
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
