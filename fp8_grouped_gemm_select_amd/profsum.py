@@ -50,7 +50,7 @@ def short_name(kernel: str) -> str:
     k = kernel
     if k.startswith("void "):
         k = k[5:]
-    for prefix in ("moe::(anonymous namespace)::", "moe::"):
+    for prefix in ("moe::(anonymous namespace)::", "moe::", "(anonymous namespace)::"):
         if k.startswith(prefix):
             k = k[len(prefix):]
     return k.split("(")[0]

@@ -35,6 +35,9 @@ def test_short_names_and_stages():
                                                       "act_requant", "gemm", "post_reorder"]
     assert profsum.stage_of("__amd_rocclr_copyBuffer") is None
     assert profsum.stage_of("void moe::(anonymous namespace)::select_rows_kernel<16>(float const*)") == "select"
+    # kernels in a top-level anonymous namespace (the ceilings library) keep their names
+    assert profsum.short_name("(anonymous namespace)::copy_kernel(HIP_vector_type<unsigned int, 4u> const*, long)") \
+        == "copy_kernel"
 
 
 def test_traffic_calibration_and_split(tmp_path):
