@@ -9,7 +9,7 @@
 // A deterministic stable counting sort over the (token, slot) pairs
 // f = t * topk + slot, in chunks of 64 consecutive pairs (one wave each):
 //   count    a pair's stable rank among the chunk's earlier pairs of the same
-//            local expert (register compares, kept in src2dst) and the
+//            local expert (one ballot per distinct expert, kept in src2dst) and the
 //            chunk's count per expert, stored expert-major [E_l][nchunks];
 //   scan     one block per local expert: an exclusive scan of its chunk
 //            counts (entry (e, c) = expert e's pairs in chunks before c) and its
@@ -88,11 +88,28 @@ __device__ __forceinline__ int local_of(int id, const LocalMap& m) {
     return -1;
 }
 
+// A local pair's stable rank among the lower lanes of its wave that hold the same
+// local expert (below) and how many lanes hold it (all); one ballot round per
+// distinct local expert present (a chunk of 64 pairs holds a few), lanes that
+// are not local (e < 0) get 0.
+__device__ __forceinline__ void chunk_rank(int e, int lane, int& below, int& all) {
+    uint64_t rem = __ballot(e >= 0);
+    while (rem) {
+        const int x = __builtin_amdgcn_readlane(e, __builtin_ctzll(rem));
+        const uint64_t m = __ballot(e == x);
+        if (e == x) {
+            below = __popcll(m & lanemask_lt(lane));
+            all = __popcll(m);
+        }
+        rem &= ~m;
+    }
+}
+
 // ---- count: chunk-local stable ranks -----------------------------------------
 // One 64-thread block per chunk of 64 pairs; lane l holds pair 64 c + l. Its
-// rank is the number of lower lanes holding the same local expert (compared
-// against every lane's expert via readlane); the lane holding an expert's last
-// occurrence in the chunk records the count. cnt[] (dynamic LDS, num_local
+// rank is the number of lower lanes holding the same local expert
+// (chunk_rank); the lane holding an expert's last occurrence in the chunk
+// records the count. cnt[] (dynamic LDS, num_local
 // ints) gives every (expert, chunk) entry exactly one writer.
 __global__ __launch_bounds__(64) void pr_count_kernel(const int32_t* __restrict__ ids, int64_t F,
                                                       LocalMap map, int num_local, int64_t nch,
@@ -106,13 +123,7 @@ __global__ __launch_bounds__(64) void pr_count_kernel(const int32_t* __restrict_
     const int e = f < F ? local_of(ids[f], map) : -1;
     const bool local = e >= 0;
     int below = 0, all = 0;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-        const int ej = __builtin_amdgcn_readlane(e, j);
-        const bool m = ej == e;
-        below += (m && j < lane) ? 1 : 0;
-        all += m ? 1 : 0;
-    }
+    chunk_rank(e, lane, below, all);
     __syncthreads();  // cnt[] cleared
     if (local && below == all - 1) cnt[e] = all;
     if (f < F) src2dst[f] = local ? below : -1;
@@ -223,13 +234,7 @@ __global__ __launch_bounds__(1024) void pr_count_scan_kernel(const int32_t* __re
         const int64_t f = (int64_t)c * kChunkPairs + lane;
         const int e = f < F ? local_of(ids[f], map) : -1;
         int below = 0, all = 0;
-#pragma unroll
-        for (int j = 0; j < 64; ++j) {
-            const int ej = __builtin_amdgcn_readlane(e, j);
-            const bool m = ej == e;
-            below += (m && j < lane) ? 1 : 0;
-            all += m ? 1 : 0;
-        }
+        chunk_rank(e, lane, below, all);
         if (e >= 0 && below == all - 1) cnt[e * nch + c] = all;
         if (f < F) src2dst[f] = e >= 0 ? below : -1;
     }
@@ -298,12 +303,14 @@ __device__ __forceinline__ uint4 quant16(const uint4& a, const uint4& b, float i
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// One token (one wave): lanes < topk hold its pairs.
+// One token (one wave): lanes < topk hold its pairs. rank[f] is pair f's stable
+// rank among its chunk's earlier pairs of the same expert (src2dst itself, as
+// the count pass left it, or the small-batch kernel's LDS copy).
 template <int MODE>
 __device__ __forceinline__ void scatter_token(
     const uint4* __restrict__ x, const int32_t* __restrict__ ids, int64_t t, int H, int topk,
     const LocalMap& map, int num_local, int64_t nch, const int32_t* __restrict__ offs,
-    const int32_t* __restrict__ tot,
+    const int32_t* __restrict__ tot, const int32_t* rank,
     int32_t* __restrict__ src2dst, int32_t* __restrict__ dst2src, uint8_t* __restrict__ a_q,
     float* __restrict__ a_scale, const float* __restrict__ tscale, int64_t m_cap, int lane) {
     const int64_t f = t * topk + lane;
@@ -339,7 +346,7 @@ __device__ __forceinline__ void scatter_token(
     const int base = expert_base(tot, num_local, e, lane, m_all);
     int dst = -1;
     if (e >= 0) {
-        dst = base + offs[(int64_t)e * nch + f / kChunkPairs] + src2dst[f];
+        dst = base + offs[(int64_t)e * nch + f / kChunkPairs] + rank[f];
         // rows past m_cap exist only if a token repeats an expert; drop them
         if (dst >= m_cap) dst = -1;
         else dst2src[dst] = (int32_t)f;
@@ -456,9 +463,91 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void p
         if (lane == 0) seg[num_local] = carry;
     }
     if (t < T)
-        scatter_token<MODE>(x, ids, t, H, topk, map, num_local, nch, offs, tot, src2dst, dst2src,
+        scatter_token<MODE>(x, ids, t, H, topk, map, num_local, nch, offs, tot, src2dst, src2dst, dst2src,
                             a_q, a_scale, tscale, m_cap, lane);
     // rows M .. m_cap-1 of dst2src are -1 (grid-stride over the whole grid)
+    for (int64_t r = M + (int64_t)blockIdx.x * 256 + threadIdx.x; r < m_cap; r += (int64_t)gridDim.x * 256)
+        dst2src[r] = -1;
+}
+
+// ---- small batches: count, scan and scatter in one launch --------------------------
+// When the pairs fill at most kSmallChunks chunks and the expert x chunk table
+// fits LDS (a decode batch), every scatter block derives the permutation
+// itself: its four waves rank the chunks exactly as the count pass does, thread
+// e scans expert e's row of the table as the scan pass does, the per-tensor
+// amax partials are reduced, and the block then scatters its four tokens as the
+// scatter kernel does. The blocks repeat the same small computation instead of
+// waiting for two earlier launches; the results are the same bits.
+constexpr int kSmallChunks = 32;    // up to 2048 pairs
+constexpr int kSmallTable = 4096;   // expert x chunk entries
+constexpr int kSmallLocal = 1024;   // local experts
+
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void pr_scatter_small_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ ids, int64_t T, int H, int topk,
+    LocalMap map, int num_local, int nch, int32_t* __restrict__ seg, int32_t* __restrict__ src2dst,
+    int32_t* __restrict__ dst2src, uint8_t* __restrict__ a_q, float* __restrict__ a_scale,
+    const float* __restrict__ amax_part, int n_part, int64_t m_cap) {
+    __shared__ int32_t s_offs[kSmallTable];                // counts, then their scan per expert
+    __shared__ int32_t s_rank[kSmallChunks * kChunkPairs];  // within-chunk ranks
+    __shared__ int32_t s_tot[kSmallLocal];
+    __shared__ float s_ts[2], s_red[4];
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+    const int64_t F = T * topk;
+    for (int i = tid; i < num_local * nch; i += 256) s_offs[i] = 0;
+    __syncthreads();
+    for (int c = wid; c < nch; c += 4) {
+        const int f = c * kChunkPairs + lane;
+        const int e = f < F ? local_of(ids[f], map) : -1;
+        int below = 0, all = 0;
+        chunk_rank(e, lane, below, all);
+        if (e >= 0 && below == all - 1) s_offs[e * nch + c] = all;
+        s_rank[f] = below;
+    }
+    __syncthreads();
+    for (int e = tid; e < num_local; e += 256) {
+        int run = 0;
+        for (int c = 0; c < nch; ++c) {
+            const int v = s_offs[e * nch + c];
+            s_offs[e * nch + c] = run;
+            run += v;
+        }
+        s_tot[e] = run;
+    }
+    if (MODE == MOE_ACT_PER_TENSOR) {
+        float m = 0.0f;
+        for (int i = tid; i < n_part; i += 256) m = fmaxf(m, amax_part[i]);
+        m = wave_max(m);
+        if (lane == 0) s_red[wid] = m;
+    }
+    __syncthreads();
+    if (MODE == MOE_ACT_PER_TENSOR && tid == 0) {
+        const float a = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+        float sc, inv;
+        dyn_scale(a, sc, inv);
+        s_ts[0] = sc;
+        s_ts[1] = inv;
+        if (blockIdx.x == 0) a_scale[0] = sc;
+    }
+    __syncthreads();
+
+    const int64_t t = (int64_t)blockIdx.x * 4 + wid;
+    int m_all = 0;
+    expert_base(s_tot, num_local, -1, lane, m_all);  // M, for the tail below
+    const int64_t M = m_all;
+    if (blockIdx.x == 0 && wid == 0) {  // seg_indptr = [first rows..., M]
+        int carry = 0;
+        for (int q0 = 0; q0 < num_local; q0 += 64) {
+            const int v = q0 + lane < num_local ? s_tot[q0 + lane] : 0;
+            const int incl = wave_inclusive_scan(v, lane);
+            if (q0 + lane < num_local) seg[q0 + lane] = incl - v + carry;
+            carry += __shfl(incl, 63, MOE_WAVE);
+        }
+        if (lane == 0) seg[num_local] = carry;
+    }
+    if (t < T)
+        scatter_token<MODE>(x, ids, t, H, topk, map, num_local, nch, s_offs, s_tot, s_rank, src2dst, dst2src,
+                            a_q, a_scale, s_ts, m_cap, lane);
     for (int64_t r = M + (int64_t)blockIdx.x * 256 + threadIdx.x; r < m_cap; r += (int64_t)gridDim.x * 256)
         dst2src[r] = -1;
 }
@@ -518,6 +607,18 @@ static int pre_reorder_impl(const void* x_bf16, const int32_t* topk_ids, int64_t
         hipLaunchKernelGGL(pr_amax_kernel, dim3(n_part), dim3(256), 0, s, (const uint4*)x_bf16,
                            n16, ws.amax_part);
     }
+    const int64_t nblk = ceil_div(T, 4) > 0 ? ceil_div(T, 4) : 1;
+    if (nch <= kSmallChunks && (int64_t)num_local * nch <= kSmallTable && num_local <= kSmallLocal) {
+#define MOE_LAUNCH_SMALL(MODE)                                                                    \
+    hipLaunchKernelGGL(pr_scatter_small_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s,     \
+                       (const uint4*)x_bf16, topk_ids, T, H, topk, map, num_local, (int)nch,      \
+                       seg_indptr, src2dst, dst2src, a_q, a_scale, ws.amax_part, n_part, m_cap)
+        if (act_quant == MOE_ACT_PER_TENSOR) MOE_LAUNCH_SMALL(MOE_ACT_PER_TENSOR);
+        else if (act_quant == MOE_ACT_PER_TOKEN) MOE_LAUNCH_SMALL(MOE_ACT_PER_TOKEN);
+        else MOE_LAUNCH_SMALL(MOE_ACT_PER_GROUP);
+#undef MOE_LAUNCH_SMALL
+        return launch_status();
+    }
     if (nch <= kFusedChunks && (int64_t)num_local * nch <= kFusedTable) {
         hipLaunchKernelGGL(pr_count_scan_kernel, dim3(1), dim3(1024), 0, s, topk_ids, T * (int64_t)topk, map,
                            num_local, (int)nch, src2dst, ws.offs, ws.tot, ws.amax_part, n_part, per_tensor,
@@ -533,7 +634,6 @@ static int pre_reorder_impl(const void* x_bf16, const int32_t* topk_ids, int64_t
     }
     // The scatter grid also writes seg_indptr and clears dst2src[M..m_cap); it
     // always runs, with at least one block.
-    const int64_t nblk = ceil_div(T, 4) > 0 ? ceil_div(T, 4) : 1;
     {
 #define MOE_LAUNCH_SCATTER(MODE)                                                                  \
     hipLaunchKernelGGL(pr_scatter_quant_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s,     \

@@ -174,8 +174,14 @@ def test_pre_reorder_workloads(name):
 
 
 @pytest.mark.parametrize("act_quant", [W.ACT_PER_TENSOR, W.ACT_PER_TOKEN, W.ACT_PER_GROUP])
+# (T, H, E, topk, expert_start, num_local). The library derives the permutation in
+# one launch for up to 2048 pairs with at most 4096 expert x chunk entries, in a
+# single count-and-scan block up to 4096 pairs, and in separate count and scan
+# passes beyond: the last four shapes sit at and past those limits.
 @pytest.mark.parametrize("shape", [(1, 16, 4, 2, 0, 8), (63, 144, 16, 4, 3, 5), (65, 9216, 8, 8, 0, 8),
-                                   (200, 256, 64, 6, 10, 20), (130, 384, 8, 2, 0, 1)])
+                                   (200, 256, 64, 6, 10, 20), (130, 384, 8, 2, 0, 1),
+                                   (256, 128, 256, 8, 0, 128), (256, 64, 256, 8, 0, 200),
+                                   (500, 256, 64, 8, 0, 64), (700, 64, 16, 6, 0, 16)])
 def test_pre_reorder_ragged(act_quant, shape):
     T, H, E, topk, start, nl = shape
     g = np.random.default_rng(T * 7 + H)
