@@ -50,8 +50,11 @@ def _run(fn_noalloc, x, ids, expert_start, num_local, act_quant):
 
 
 # (T, H, E, topk, expert_start, num_local, act_quant): the first call is the
-# DeepSeek-V3 prefill share's shape; each later call is smaller than the first
+# DeepSeek-V3 prefill share's shape; each later call is smaller than the first.
+# The calls take each way of forming the permutation: separate count and scan
+# passes, one count-and-scan block (2048-4096 pairs), one launch (fewer).
 CALLS = [(8192, 7168, 256, 8, 0, 32, W.ACT_PER_TOKEN),
+         (600, 384, 64, 6, 4, 48, W.ACT_PER_TOKEN),
          (300, 512, 64, 6, 8, 40, W.ACT_PER_GROUP),
          (77, 256, 16, 4, 0, 16, W.ACT_PER_TENSOR)]
 
