@@ -19,6 +19,8 @@
 //            prefix sum of the totals, block 0 writes them out; final rows,
 //            dst2src, and the quantised row written to each of the token's
 //            local rows; the grid clears dst2src[M..m_cap).
+// Batches of up to 4096 pairs count and scan in one block; up to 2048 pairs,
+// every scatter block counts and scans for itself and the stage is one launch.
 #include "common.h"
 
 #include <mutex>
