@@ -152,6 +152,40 @@ __global__ __launch_bounds__(256) void act_requant_kernel(const uint16_t* __rest
     }
 }
 
+// Per-group mode when a row's 16-column chunks do not fill whole waves (I / 16
+// not a multiple of 64, e.g. I = 768, where one wave per row leaves a quarter of
+// its lanes idle): the chunks of all rows are numbered row-major and each wave
+// takes 64 consecutive ones, so no lane idles. A 128-column group is 8
+// consecutive chunks of one row (I is a multiple of 128 here), so the group
+// maximum stays an 8-lane reduction; lanes past the last chunk form whole
+// groups of their own. Same values and scales as act_requant_kernel.
+__global__ __launch_bounds__(256) void act_requant_group_flat_kernel(const uint16_t* __restrict__ gu,
+                                                                     const int32_t* __restrict__ seg,
+                                                                     int num_local, int64_t m_cap, int I,
+                                                                     uint8_t* __restrict__ a_q,
+                                                                     float* __restrict__ a_scale) {
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t M = rows_present(seg, num_local, m_cap);
+    const int cpr = I / 16;  // chunks per row, a multiple of 8
+    const int G = I / MOE_QB;
+    const int64_t total = M * cpr;
+    for (int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 64; base < total; base += (int64_t)gridDim.x * 256) {
+        const int64_t t = base + lane;
+        const bool ok = t < total;
+        const int64_t row = ok ? t / cpr : 0;
+        const int c = ok ? (int)(t - row * cpr) * 16 : I;  // c = I: no columns (zeros)
+        const GU16 v = load_gu16(gu, row, I, c);
+        uint4 h0, h1;
+        silu_mul16_from(v, I, c, h0, h1);
+        float s, inv;
+        dyn_scale(group8_max(amax16(h0, h1)), s, inv);
+        if (ok) {
+            *(uint4*)(a_q + row * I + c) = quant16(h0, h1, inv);
+            if ((lane & 7) == 0) a_scale[row * G + c / MOE_QB] = s;
+        }
+    }
+}
+
 // Rows wider than 8192 columns (per token / per group): streamed, two passes
 // over the row for the per-token maximum.
 template <int MODE>
@@ -296,8 +330,16 @@ extern "C" int moe_act_requant(const void* gateup_bf16, const int32_t* seg_indpt
                            seg_indptr, num_local, m_cap, I, part, kActBlocks, a_q, a_scale);
         return launch_status();
     }
-    int64_t grid = ceil_div(m_cap, 4);
     const int64_t cap = (int64_t)device_cu_count() * 16;
+    if (act_quant == MOE_ACT_PER_GROUP && I % MOE_QB == 0 && (I / 16) % 64 != 0) {
+        int64_t g = ceil_div(ceil_div(m_cap * (I / 16), 64), 4);  // blocks of four 64-chunk waves
+        if (g > cap) g = cap;
+        if (g < 1) g = 1;
+        hipLaunchKernelGGL(act_requant_group_flat_kernel, dim3((unsigned)g), dim3(256), 0, s, gu, seg_indptr,
+                           num_local, m_cap, I, a_q, a_scale);
+        return launch_status();
+    }
+    int64_t grid = ceil_div(m_cap, 4);
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
     const int nit = (int)ceil_div(I, 1024);

@@ -506,8 +506,10 @@ def test_grouped_gemm_seg_clamped(path):
 # ---- stage 4 ------------------------------------------------------------------------
 
 @pytest.mark.parametrize("act_quant", [W.ACT_PER_TENSOR, W.ACT_PER_TOKEN, W.ACT_PER_GROUP])
+# In the per-group mode, I / 16 not a multiple of 64 (768, 384, 1152) takes the
+# kernel that packs 16-column chunks of several rows into each wave.
 @pytest.mark.parametrize("dims", [((20, 0, 31), 64), ((300, 17), 2048), ((5,), 9216), ((64, 64), 768),
-                                  ((7, 3), 3072), ((9,), 5120)])
+                                  ((7, 3), 3072), ((9,), 5120), ((13, 0, 6), 384), ((1, 40, 2), 1152)])
 def test_act_requant_ragged(act_quant, dims):
     counts, I = dims
     g = np.random.default_rng(len(counts) * 100 + I)
