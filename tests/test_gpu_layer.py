@@ -179,6 +179,25 @@ def test_layer_single_token(act_quant, w_quant, w_fp4, seed):
     G.assert_close_layer(G.bf16_bits(buf.out), ref["out"], what="layer output")
 
 
+@pytest.mark.parametrize("T,num_routed", [(40, 0), (1, 6), (1, 0)])
+def test_layer_shared_expert_edges(T, num_routed):
+    """A shared expert with no routed expert local to this GPU (every row is the
+    shared expert's), and a single token with and without routed local experts:
+    ids, permutation and stage-2 codes bit-exact, the output within tolerance."""
+    cfg = dataclasses.replace(shared_cfg(), T=T, num_local=num_routed, expert_start=5 if num_routed else 16)
+    inp = W.gen_layer_inputs(cfg, seed=4)
+    ref = oracle.layer(inp)
+    M = int(ref["seg_indptr"][-1])
+    print(f"layer shared edges T={T} routed local={num_routed} M={M}", flush=True)
+    buf = run_layer(inp)
+    assert np.array_equal(buf.topk_ids.cpu().numpy(), ref["ids"])
+    assert np.array_equal(buf.seg_indptr.cpu().numpy(), ref["seg_indptr"])
+    assert np.array_equal(buf.src2dst.cpu().numpy(), ref["src2dst"])
+    assert np.array_equal(buf.dst2src.cpu().numpy(), ref["dst2src"])
+    assert np.array_equal(buf.a13.cpu().numpy()[:M], ref["a13"][:M])
+    G.assert_close_layer(G.bf16_bits(buf.out), ref["out"], what="layer output")
+
+
 def e4m3_ordinal(codes):
     """Signed position of an e4m3 code on the number line (codes are sign-magnitude)."""
     c = np.asarray(codes).astype(np.int32)
